@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Benchmark of the tile-pipelined GEMM chain on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
+
+A step is one single-batch evaluation of the whole chain in pipelined mode
+(scoreboard/queue reset + one persistent launch) on inputs already resident
+in HBM.  W untimed steps, then exactly K timed steps between two device
+synchronisations.  Prints one JSON line on stdout; progress goes to stderr.
+
+Also measured (outside the timed region): the worker kernel's own duration
+from HIP events recorded inside the library on the launch stream, the
+sequential and best micro-batched baselines, cold-cache latencies, and the
+CPU oracle on a bounded row sample (the CPU baseline).
+"""
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 matrix
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "single-batch chained-GEMM latency (µs) + TFLOP/s, % bf16 MFMA peak, 1 GPU"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c3")
+    ap.add_argument("--tile", default=None, help="override tile, e.g. 256x128")
+    ap.add_argument("--reps", type=int, default=20, help="reps per mode for the baseline comparison")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-modes", action="store_true", help="skip the baseline-mode comparison")
+    ap.add_argument("--profile", action="store_true",
+                    help="short run for a profiler: timed steps only, plus a 1 GiB copy kernel "
+                         "used to calibrate the traffic counters")
+    ap.add_argument("--cpu-sample-rows", type=int, default=0)
+    return ap.parse_args()
+
+
+def traffic_from_profile(workload, tile):
+    """HBM bytes per launch of the worker kernel from the committed rocprofv3
+    counter summary, or None if absent or taken on a different kernel source."""
+    from tile_dependency_pipelined_amd import profiling
+    return profiling.load_traffic(os.path.join(ROOT, "profiles"), workload, tile)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        log(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+            "the multi-GPU layer pipeline is not built.")
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from tile_dependency_pipelined_amd import chain as ch
+    from tile_dependency_pipelined_amd import inputs as gen
+    from tile_dependency_pipelined_amd import native as nat
+    from tile_dependency_pipelined_amd import tuning
+
+    if not torch.cuda.is_available():
+        log("bench.py: no GPU visible")
+        sys.exit(1)
+    cfg = gen.CONFIGS[args.workload]
+    tile = tuple(int(x) for x in args.tile.split("x")) if args.tile else tuning.TILES[args.workload]
+    log(f"workload {cfg.key}: {cfg.description}; tile {tile}")
+    t0 = time.time()
+    X, Ws = gen.config_inputs(cfg)
+    log(f"inputs generated in {time.time() - t0:.1f}s")
+    dX = ch.to_device(X, cfg.dtype)
+    dW = [ch.to_device(w, cfg.dtype) for w in Ws]
+    dY = torch.empty((cfg.M, cfg.widths[-1]), dtype=ch.DTYPES[cfg.dtype], device="cuda")
+    torch.cuda.synchronize()
+
+    plan = ch.Chain(cfg.M, cfg.widths, cfg.dtype, tile[0], tile[1], acts=list(cfg.acts))
+    stream = torch.cuda.current_stream()
+
+    def step(mode="pipelined", mb=0):
+        plan.run(dX, dW, dY, mode=mode, microbatch_rows=mb, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    st = plan.stats()
+    assert st["status"] == 0 and st["nonzero_scores"] == 0 and st["queue_is_perm"] == 1, st
+
+    # ---- timed region: exactly K steps between two synchronisations
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    w1 = time.perf_counter()
+    wall_ms = (w1 - w0) * 1e3 / args.steps
+    ev_ms = ev0.elapsed_time(ev1) / args.steps
+    log(f"timed: {args.steps} steps, {wall_ms * 1e3:.1f} us/step wall, {ev_ms * 1e3:.1f} us/step events")
+
+    # worker kernel alone (HIP events on the launch stream, inside the library)
+    kern, runs = [], []
+    for _ in range(args.steps):
+        step()
+        s = plan.stats()
+        kern.append(s["last_kernel_ms"])
+        runs.append(s["last_run_ms"])
+    kernel_ms = statistics.mean(kern)
+    log(f"worker kernel {kernel_ms * 1e3:.1f} us mean, run {statistics.mean(runs) * 1e3:.1f} us mean")
+
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == gen.BF16 else PEAK_FP32_TFLOPS
+    flops = cfg.flops
+    tflops = flops / (ev_ms * 1e-3) / 1e12
+    kernel_tflops = flops / (kernel_ms * 1e-3) / 1e12
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ev_ms, 4),
+        "latency_us": round(ev_ms * 1e3, 1),
+        "pct_peak": round(100 * tflops / peak, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == gen.BF16 else "f32",
+        "data": "synthetic (seeded N(0, sigma^2), PCG64)",
+        "config": {"workload": cfg.description, "key": cfg.key, "M": cfg.M,
+                   "widths": list(cfg.widths), "tile": list(tile), "mode": "pipelined",
+                   "workers": plan.n_workers, "tiles": plan.n_tiles},
+        "wall_ms_per_step": round(wall_ms, 4),
+    }
+
+    if args.profile:
+        # calibration copy of exactly 1 GiB for the traffic counters
+        a = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
+        b = torch.empty_like(a)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    traffic = traffic_from_profile(cfg.key, tile)
+    bound = "mfma"
+    result["roofline"] = {
+        "bound": bound, "achieved": round(kernel_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+        "frac": round(kernel_tflops / peak, 4),
+        "traffic": traffic,
+        "kernel": "cp::worker_kernel<Bf16Body<%d,%d>>" % tile if cfg.dtype == gen.BF16 else "worker_kernel<F32Body>",
+        "kernel_us": round(kernel_ms * 1e3, 1),
+        "algorithmic_flop_per_launch": flops,
+        "algorithmic_bytes_min": cfg.min_bytes(),
+        "hbm_frac_min_bytes": round(cfg.min_bytes() / (kernel_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+    }
+
+    if not args.no_modes and not args.profile:
+        result["modes"] = compare_modes(plan, step, stream, cfg, tile, args.reps, torch, tuning)
+
+    if not args.no_cpu_baseline and not args.profile:
+        result["cpu_baseline"] = cpu_baseline(cfg, X, Ws, args.cpu_sample_rows)
+
+    plan.close()
+    print(json.dumps(result), flush=True)
+
+
+def compare_modes(plan, step, stream, cfg, tile, reps, torch, tuning):
+    """Median event-timed latency of each mode, warm (back to back) and cold
+    (a 1 GiB device write between reps, outside the timed span)."""
+    scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+
+    def timed(mode, mb, cold):
+        ts = []
+        for _ in range(3):
+            step(mode, mb)
+        for _ in range(reps):
+            if cold:
+                scrub.fill_(1.0)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step(mode, mb)
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        ts.sort()
+        return {"median_us": round(statistics.median(ts), 1), "min_us": round(ts[0], 1),
+                "p10_us": round(ts[len(ts) // 10], 1), "p90_us": round(ts[(9 * len(ts)) // 10], 1)}
+
+    out = {}
+    for cold in (False, True):
+        tag = "cold" if cold else "warm"
+        out[f"pipelined_{tag}"] = timed("pipelined", 0, cold)
+        out[f"sequential_{tag}"] = timed("sequential", 0, cold)
+        best = None
+        sweep = {}
+        for m in tuning.chunk_sweep(cfg.M, tile[0]):
+            r = timed("microbatch", m, cold)
+            sweep[str(m)] = r["median_us"]
+            if best is None or r["median_us"] < best[1]["median_us"]:
+                best = (m, r)
+        if best:
+            out[f"microbatch_best_{tag}"] = dict(best[1], chunk_rows=best[0])
+            out[f"microbatch_sweep_{tag}"] = sweep
+        log(tag, {k: v for k, v in out.items() if k.endswith(tag)})
+    del scrub
+    return out
+
+
+def cpu_baseline(cfg, X, Ws, rows):
+    """The CPU oracle (fp64, as it stands) on a bounded row sample; scaled to
+    the whole batch through row independence."""
+    import numpy as np
+    import oracle
+    if rows <= 0:
+        # about 10 s of CPU work at ~1 GFLOP/s per thread
+        per_row = cfg.flops / cfg.M
+        rows = int(max(1, min(cfg.M, 10e9 * oracle.num_threads() / per_row)))
+    sel = np.arange(rows, dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.chain(X, Ws, cfg.dtype, acts=list(cfg.acts), rows=sel)
+    dt = time.perf_counter() - t0
+    flops = cfg.flops * rows / cfg.M
+    log(f"cpu oracle: {rows} rows in {dt:.2f}s ({flops / dt / 1e9:.2f} GFLOP/s)")
+    return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "sample": f"first {rows} of {cfg.M} rows of X through the whole chain "
+                                        f"({dt:.2f} s)",
+            "latency_us_whole_batch_extrapolated": round(dt * cfg.M / rows * 1e6, 0)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,180 @@
+/*
+ * cp_chain.h -- C ABI of the tile-pipelined dependent-GEMM chain for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation (CTA-Pipelining: A Latency-Oriented Spatial Scaling Method for
+ * Multi-GPU Systems, arXiv 2607.07862):
+ *   Y = ((X . W1) . W2) ... . WL          (§III-B running example: a two-layer
+ *                                         GEMM whose first output feeds the
+ *                                         second; §IV-A: one GEMM per layer;
+ *                                         §IV-B: Y = X A B)
+ * computed in output tiles.  A tile of layer l+1 starts as soon as every
+ * tile of layer l that it reads has been stored, instead of waiting for a
+ * kernel boundary (§III, execution model; Fig. 1).  Readiness is tracked by a
+ * host-built dependency array, a device scoreboard of atomic counters that
+ * producer epilogues decrement after a release fence, and a work-queue into
+ * which the producer that completes a consumer's count pushes the consumer's
+ * tile ID; a consumer prologue takes queue slots in order and remaps its
+ * workgroup to the tile it dequeued (§III-A "dependency structure"; the
+ * pith.science review, "What carries the argument").
+ *
+ * Conventions common to every entry point:
+ *   - every function returns CP_OK (0) or a negative CP_ERR_* code; no C++
+ *     exception crosses the ABI; cp_chain_last_error() gives a thread-local
+ *     detail string for the most recent failure on the calling thread;
+ *   - all matrices are dense and row-major with no padding: X[M][K0],
+ *     W_l[K_{l-1}][N_l], Y[M][N_L]; element type is the plan's dtype
+ *     (CP_F32: IEEE binary32; CP_BF16: bfloat16 bit patterns, accumulated in
+ *     fp32 and rounded to nearest-even when stored, §III-C);
+ *   - X, W[] and Y are DEVICE pointers owned by the caller; the library never
+ *     frees or retains them past the call that uses them;
+ *   - the plan owns its dependency table, scoreboard, queue, intermediates,
+ *     internal streams and events, and frees them in cp_chain_destroy.
+ */
+#ifndef CP_CHAIN_H
+#define CP_CHAIN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct cp_chain cp_chain; /* opaque plan */
+
+/* element types */
+#define CP_F32 0
+#define CP_BF16 1
+
+/* activation applied to the fp32 accumulator of a layer, before rounding */
+#define CP_ACT_NONE 0
+#define CP_ACT_GELU_TANH 1 /* x/2 (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) */
+
+/* execution modes of cp_chain_run */
+#define CP_MODE_PIPELINED 0  /* one persistent launch, tile dependencies   */
+#define CP_MODE_SEQUENTIAL 1 /* one launch per layer (kernel boundaries)   */
+#define CP_MODE_MICROBATCH 2 /* M split into chunks over two streams       */
+
+/* status codes */
+#define CP_OK 0
+#define CP_ERR_INVALID_ARG (-1)
+#define CP_ERR_SHAPE (-2)
+#define CP_ERR_UNSUPPORTED (-3)
+#define CP_ERR_OOM (-4)
+#define CP_ERR_HIP (-5)
+#define CP_ERR_TIMEOUT (-6)
+#define CP_ERR_NO_DEVICE (-7)
+#define CP_ERR_INVARIANT (-8)
+
+/* plan flags (bitmask) */
+#define CP_FLAG_DEBUG 1u        /* count dequeues per tile; enables invariant checks in stats */
+#define CP_FLAG_TRACE 2u        /* per-tile timestamps (100 MHz wall clock)                  */
+#define CP_FLAG_POISON 4u       /* fill intermediates with NaN before every run              */
+#define CP_FLAG_DELAY_INJECT 8u /* a fixed pseudo-random quarter of producers stall ~20 us   */
+/* test only: the last tile's in-degree is raised by one so that it never
+ * becomes ready; the worker holding its slot gives up after 50 ms (instead of
+ * the default 2 s), sets CP_ERR_TIMEOUT and every worker exits.  Needs L >= 2. */
+#define CP_FLAG_STARVE_LAST 16u
+
+#define CP_MAX_LAYERS 8
+
+/* Statistics and invariants of the most recent run on a plan. */
+typedef struct cp_chain_stats_t {
+    int32_t status;          /* CP_OK, or CP_ERR_TIMEOUT if a worker's wait expired        */
+    int32_t mode;            /* mode of the last run                                      */
+    int32_t n_tiles;         /* T: tiles over all layers                                  */
+    int32_t n_first;         /* P1: tiles of layer 1 (pre-filled into the queue)          */
+    int32_t n_edges;         /* E: dependency edges = scoreboard decrements per run       */
+    int32_t n_workers;       /* persistent workgroups launched (pipelined mode)           */
+    int32_t tile_m, tile_n;  /* tile shape                                                */
+    /* invariants, valid after a pipelined run (dequeue counts need CP_FLAG_DEBUG):      */
+    int32_t nonzero_scores;  /* consumers whose counter did not end at 0                  */
+    int32_t bad_dequeues;    /* tiles not dequeued exactly once (-1 if not recorded)      */
+    int32_t queue_is_perm;   /* 1 if queue[0..T) is a permutation of [0,T)                */
+    uint32_t head, tail;     /* final ticket counter (>= T) and push counter (== T)        */
+    int32_t order_violations;/* TRACE only: consumers that started before a producer ended */
+    double last_run_ms;      /* elapsed time of the last run, from events on its stream   */
+    double last_kernel_ms;   /* pipelined: the persistent launch alone (reset excluded);
+                                other modes: same as last_run_ms                          */
+} cp_chain_stats_t;
+
+/*
+ * cp_chain_plan -- validate a chain shape and build everything a run needs.
+ *   out       receives the plan (set to NULL on failure)
+ *   M         rows of X (the "input sequence length", §IV-A); M % tile_m == 0
+ *   n_layers  L, 1 <= L <= CP_MAX_LAYERS
+ *   widths    L+1 entries K0, N1, ..., NL; every N_l % tile_n == 0, and every
+ *             contraction length K_{l-1} a multiple of 64 (bf16) or 32 (fp32)
+ *   dtype     CP_F32 or CP_BF16
+ *   tile_m,n  output tile of one workgroup (one CTA, §III).  bf16: each of
+ *             64, 128, 256; fp32: 64 x 64.  Other tiles: CP_ERR_UNSUPPORTED.
+ *   acts      L activation codes (after each layer), or NULL for none
+ *   flags     CP_FLAG_* bitmask
+ * Builds the dependency array on the host -- consumer tile (l+1, i, j) waits
+ * on all tiles (l, i, k) of row-block i, derived from the static tile dataflow
+ * of the GEMM (§III-A; review, "Circularity Check") -- uploads it, allocates the
+ * scoreboard, queue, intermediates C_1..C_{L-1} (M x N_l each) and sizes the
+ * persistent grid from occupancy.  Needs a HIP device (CP_ERR_NO_DEVICE).
+ */
+int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *widths,
+                  int32_t dtype, int32_t tile_m, int32_t tile_n, const int32_t *acts,
+                  uint32_t flags);
+
+/*
+ * cp_chain_run -- enqueue one evaluation of the chain on `stream`
+ * (a hipStream_t; NULL means the default stream) and return.
+ *   X, W[0..L-1], Y   device pointers as described above
+ *   mode              CP_MODE_*; all modes run the same tile body and produce
+ *                     bit-identical Y (the original kernel is preserved, §III-C)
+ *   microbatch_rows   CP_MODE_MICROBATCH only: rows per chunk, a multiple of
+ *                     tile_m dividing M (the static micro-batching baseline's
+ *                     "chunk size", §IV-A); ignored otherwise
+ * Pipelined mode resets the scoreboard/queue on the stream, then launches one
+ * persistent grid.  At most one run may be in flight per plan.  A device-side
+ * watchdog expiry is reported by cp_chain_stats (status CP_ERR_TIMEOUT).
+ */
+int cp_chain_run(cp_chain *plan, const void *X, const void *const *W, void *Y,
+                 void *stream, int32_t mode, int64_t microbatch_rows);
+
+/*
+ * cp_chain_stats -- synchronise with the plan's last run and report status,
+ * timing and the scoreboard/queue invariants (every
+ * counter ends at 0, every tile dequeued exactly once).
+ */
+int cp_chain_stats(cp_chain *plan, cp_chain_stats_t *out);
+
+/*
+ * cp_chain_trace -- copy the per-tile timestamps of the last pipelined run
+ * (plan built with CP_FLAG_TRACE) into host memory `out` of 4*T uint64:
+ * [ticket taken, tile dequeued (ready), GEMM body done, stores released] in
+ * 100 MHz wall-clock ticks -- the epilogue/visibility/prologue phases of the
+ * paper's Fig. 2.  CP_ERR_INVALID_ARG without the flag.
+ */
+int cp_chain_trace(cp_chain *plan, uint64_t *out, int64_t capacity);
+
+/* cp_chain_destroy -- wait for the plan's work and free it.  NULL is a no-op. */
+int cp_chain_destroy(cp_chain *plan);
+
+/*
+ * cp_chain_tile_graph -- host-only: the dependency array a plan of this shape
+ * would use, without touching a device.  Pass NULL arrays to query sizes.
+ *   n_tiles, n_edges         out: T and E
+ *   layer_off[L+1]           first flat tile ID of each layer, then T
+ *   indeg[T]                 initial scoreboard value per tile (0 for layer 1)
+ *   dep_off[T+1], dep_ids[E] CSR producer -> consumers
+ * Flat IDs list each layer's tiles row-block-major: id = off_l + i*(N_l/tile_n) + j.
+ */
+int cp_chain_tile_graph(int64_t M, int32_t n_layers, const int64_t *widths, int32_t tile_m,
+                        int32_t tile_n, int32_t *n_tiles, int32_t *n_edges, int32_t *layer_off,
+                        int32_t *indeg, int32_t *dep_off, int32_t *dep_ids);
+
+/* static description of a status code */
+const char *cp_chain_error_string(int code);
+/* thread-local detail of the most recent failure on this thread ("" if none) */
+const char *cp_chain_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CP_CHAIN_H */

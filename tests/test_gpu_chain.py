@@ -1,0 +1,275 @@
+"""GPU parity tests: the HIP path, called through the C ABI, against the CPU
+oracle on the same seeded inputs; bit-exact agreement between the pipelined,
+sequential and micro-batched modes; exact scoreboard/queue invariants.
+
+Tolerances: max|err|/max|ref| <= 1e-4 for fp32 chains and <= 2e-2 for bf16
+chains (fp32 accumulation, bf16 storage of every intermediate)."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from tile_dependency_pipelined_amd import inputs as gen
+from tile_dependency_pipelined_amd import tuning
+
+pytestmark = pytest.mark.gpu
+
+TOL = {gen.F32: 1e-4, gen.BF16: 2e-2}
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def rt():
+    import torch
+    from tile_dependency_pipelined_amd import chain, native
+    assert torch.cuda.is_available()
+    torch.cuda.init()
+    return {"torch": torch, "chain": chain, "nat": native}
+
+
+def run_modes(rt, X, Ws, dtype, tile, acts=None, flags=0, modes=("pipelined", "sequential"),
+              mb_rows=None, reps=1):
+    """Run the chain in each mode; return {mode: host Y} and the pipelined stats."""
+    torch, ch, nat = rt["torch"], rt["chain"], rt["nat"]
+    M = X.shape[0]
+    widths = [X.shape[1]] + [w.shape[1] for w in Ws]
+    dX = ch.to_device(X, dtype)
+    dW = [ch.to_device(w, dtype) for w in Ws]
+    out, stats = {}, None
+    with ch.Chain(M, widths, dtype, tile[0], tile[1], acts=acts, flags=flags) as c:
+        for mode in modes:
+            for rep in range(reps):
+                dY = torch.full((M, widths[-1]), float("nan"), dtype=ch.DTYPES[dtype], device="cuda")
+                c.run(dX, dW, dY, mode=mode,
+                      microbatch_rows=(mb_rows or tile[0]) if mode == "microbatch" else 0)
+                st = c.stats()
+                assert st["status"] == 0, st
+                if mode == "pipelined":
+                    check_invariants(st, flags)
+                    stats = st
+                y = ch.to_host(dY, dtype)
+                if rep == 0:
+                    out[mode] = y
+                else:
+                    assert np.array_equal(y.view(np.uint32 if dtype == gen.F32 else np.uint16),
+                                          out[mode].view(np.uint32 if dtype == gen.F32 else np.uint16)), \
+                        f"{mode} rep {rep} differs"
+    return out, stats
+
+
+def check_invariants(st, flags):
+    T = st["n_tiles"]
+    assert st["nonzero_scores"] == 0, st
+    assert st["queue_is_perm"] == 1, st
+    assert st["tail"] == T, st
+    assert st["head"] >= T, st
+    if flags & rt_flags()["DEBUG"]:
+        assert st["bad_dequeues"] == 0, st
+    if flags & rt_flags()["TRACE"]:
+        assert st["order_violations"] == 0, st
+
+
+def rt_flags():
+    from tile_dependency_pipelined_amd import native as nat
+    return {"DEBUG": nat.CP_FLAG_DEBUG, "TRACE": nat.CP_FLAG_TRACE, "POISON": nat.CP_FLAG_POISON,
+            "DELAY": nat.CP_FLAG_DELAY_INJECT}
+
+
+def as_values(y, dtype):
+    return oracle.bf16_to_f64(y) if dtype == gen.BF16 else y.astype(np.float64)
+
+
+def same_bits(a, b):
+    return np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def all_flags():
+    f = rt_flags()
+    return f["DEBUG"] | f["TRACE"] | f["POISON"]
+
+
+# ----------------------------------------------------------------------------- fp32
+
+def test_c1_fp32_parity_all_modes(rt):
+    cfg = gen.CONFIGS["c1"]
+    X, Ws = gen.config_inputs(cfg)
+    say("c1: fp32 128x512x512x512, tile", cfg.tile)
+    out, st = run_modes(rt, X, Ws, cfg.dtype, cfg.tile, flags=all_flags(),
+                        modes=("pipelined", "sequential", "microbatch"), mb_rows=64, reps=3)
+    ref = oracle.chain(X, Ws, cfg.dtype)
+    err = oracle.rel_err(as_values(out["pipelined"], cfg.dtype), ref)
+    say("c1 rel err", err, "stats", st)
+    assert err <= TOL[gen.F32]
+    assert same_bits(out["pipelined"], out["sequential"])
+    assert same_bits(out["pipelined"], out["microbatch"])
+    assert st["n_tiles"] == 32 and st["n_edges"] == 128
+
+
+# ----------------------------------------------------------------------------- bf16 small
+
+BF16_TILES = [(256, 256), (256, 128), (128, 256), (128, 128), (256, 64), (64, 256), (128, 64),
+              (64, 128), (64, 64)]
+
+
+@pytest.mark.parametrize("tile", BF16_TILES, ids=[f"{a}x{b}" for a, b in BF16_TILES])
+def test_bf16_small_parity(rt, tile):
+    bm, bn = tile
+    M = 3 * bm
+    widths = (320, 3 * bn, 2 * bn)
+    say("bf16 small", tile, M, widths)
+    X, Ws = gen.chain_inputs(M, widths, gen.BF16, 1.0, (1 / np.sqrt(320), 1 / np.sqrt(3 * bn)), 50)
+    out, st = run_modes(rt, X, Ws, gen.BF16, tile, flags=all_flags(),
+                        modes=("pipelined", "sequential", "microbatch"), mb_rows=bm)
+    ref = oracle.chain(X, Ws, gen.BF16)
+    err = oracle.rel_err(as_values(out["pipelined"], gen.BF16), ref)
+    say("rel err", err)
+    assert err <= TOL[gen.BF16]
+    assert same_bits(out["pipelined"], out["sequential"])
+    assert same_bits(out["pipelined"], out["microbatch"])
+
+
+@pytest.mark.parametrize("dtype", [gen.F32, gen.BF16], ids=["f32", "bf16"])
+def test_signed_permutation_chain_exact_with_poison(rt, dtype):
+    """X . P1 D1 . P2 D2 . P3 D3 is exact in every element type, so the GPU
+    result must equal the oracle bit for bit; intermediates are NaN-poisoned
+    before every run and a quarter of producers are delayed, so a consumer
+    that read an intermediate before its producers published would show."""
+    f = rt_flags()
+    tile = (64, 64) if dtype == gen.F32 else (128, 128)
+    n = 512 if dtype == gen.F32 else 1024
+    M = 4 * tile[0]
+    X = gen.normal_matrix((M, n), 1.0, 60, dtype)
+    Ws = [gen.signed_permutation(n, 61 + l, dtype, scale_pow2=s) for l, s in enumerate((1, -2, 0))]
+    say("perm chain", dtype, tile, M, n)
+    out, st = run_modes(rt, X, Ws, dtype, tile, flags=all_flags() | f["DELAY"],
+                        modes=("pipelined", "sequential"), reps=3)
+    ref = oracle.chain(X, Ws, dtype)
+    assert np.array_equal(as_values(out["pipelined"], dtype), ref)
+    assert np.array_equal(as_values(out["sequential"], dtype), ref)
+
+
+def test_gelu_chain_small(rt):
+    M, widths = 128, (256, 512, 256)
+    X, Ws = gen.chain_inputs(M, widths, gen.BF16, 1.0, (1 / 16, 1 / np.sqrt(512)), 70)
+    acts = [gen.ACT_GELU_TANH, gen.ACT_NONE]
+    out, _ = run_modes(rt, X, Ws, gen.BF16, (64, 128), acts=acts, flags=all_flags())
+    ref = oracle.chain(X, Ws, gen.BF16, acts=acts)
+    err = oracle.rel_err(as_values(out["pipelined"], gen.BF16), ref)
+    say("gelu rel err", err)
+    assert err <= TOL[gen.BF16]
+    assert same_bits(out["pipelined"], out["sequential"])
+
+
+# ----------------------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("case", [
+    ("one tile, one layer", 64, (64, 64), (64, 64)),
+    ("one layer", 256, (512, 1024), (128, 128)),
+    ("single row-block", 128, (256, 512, 256), (128, 128)),
+    ("eight layers", 256, (128, 256, 128, 256, 128, 256, 128, 256, 128), (64, 128)),
+    ("widening and narrowing", 192, (64, 448, 64, 192), (64, 64)),
+    ("fewer tiles than CUs", 128, (128, 128, 128), (128, 128)),
+], ids=lambda c: c[0])
+def test_edge_shapes(rt, case):
+    name, M, widths, tile = case
+    L = len(widths) - 1
+    stds = tuple(1 / np.sqrt(widths[l]) for l in range(L))
+    X, Ws = gen.chain_inputs(M, widths, gen.BF16, 1.0, stds, 80)
+    say("edge", name)
+    out, st = run_modes(rt, X, Ws, gen.BF16, tile, flags=all_flags())
+    ref = oracle.chain(X, Ws, gen.BF16)
+    err = oracle.rel_err(as_values(out["pipelined"], gen.BF16), ref)
+    assert err <= TOL[gen.BF16], err
+    assert same_bits(out["pipelined"], out["sequential"])
+
+
+def test_many_tiles_many_waves(rt):
+    """More tiles than workers, ragged last wave (T % workers != 0)."""
+    M, widths = 1536, (512, 1088 + 64 * 3, 576)   # 24 row-blocks of 64
+    X, Ws = gen.chain_inputs(M, widths, gen.BF16, 1.0, (1 / np.sqrt(512), 1 / np.sqrt(1280)), 81)
+    out, st = run_modes(rt, X, Ws, gen.BF16, (64, 64), flags=all_flags(), reps=2)
+    say("workers", st["n_workers"], "tiles", st["n_tiles"])
+    assert st["n_tiles"] % st["n_workers"] != 0
+    ref = oracle.chain(X, Ws, gen.BF16)
+    assert oracle.rel_err(as_values(out["pipelined"], gen.BF16), ref) <= TOL[gen.BF16]
+    assert same_bits(out["pipelined"], out["sequential"])
+
+
+def test_rejects_bad_shapes_on_device(rt):
+    nat = rt["nat"]
+    with pytest.raises(nat.CpError) as e:
+        nat.cp_chain_plan(100, [256, 256], nat.CP_BF16, 64, 64)
+    assert e.value.code == nat.CP_ERR_SHAPE
+
+
+def test_watchdog_timeout_is_reported(rt):
+    """A consumer that never becomes ready ends the run through the worker's
+    own bounded wait (50 ms with this test flag) with CP_ERR_TIMEOUT."""
+    torch, ch, nat = rt["torch"], rt["chain"], rt["nat"]
+    M, widths = 128, (128, 128, 128)
+    X, Ws = gen.chain_inputs(M, widths, gen.BF16, 1.0, (0.1, 0.1), 90)
+    dX, dW = ch.to_device(X, gen.BF16), [ch.to_device(w, gen.BF16) for w in Ws]
+    dY = torch.empty((M, 128), dtype=torch.bfloat16, device="cuda")
+    with ch.Chain(M, widths, gen.BF16, 64, 64, flags=nat.CP_FLAG_STARVE_LAST | nat.CP_FLAG_DEBUG) as c:
+        c.run(dX, dW, dY)
+        st = c.stats(check=False)
+        say("watchdog stats", st)
+        assert st["rc"] == nat.CP_ERR_TIMEOUT and st["status"] == nat.CP_ERR_TIMEOUT
+        assert st["tail"] == st["n_tiles"] - 1
+        # the plan is reusable afterwards in the other modes
+        c.run(dX, dW, dY, mode="sequential")
+        assert c.stats()["status"] == 0
+
+
+# ----------------------------------------------------------------------------- workloads
+
+def test_c2_full_parity(rt):
+    cfg = gen.CONFIGS["c2"]
+    tile = tuning.TILES["c2"]
+    X, Ws = gen.config_inputs(cfg)
+    say("c2 full, tile", tile)
+    out, st = run_modes(rt, X, Ws, cfg.dtype, tile, flags=all_flags(),
+                        modes=("pipelined", "sequential", "microbatch"), mb_rows=256)
+    ref = oracle.chain(X, Ws, cfg.dtype)
+    err = oracle.rel_err(as_values(out["pipelined"], cfg.dtype), ref)
+    say("c2 rel err", err)
+    assert err <= TOL[gen.BF16]
+    assert same_bits(out["pipelined"], out["sequential"])
+    assert same_bits(out["pipelined"], out["microbatch"])
+
+
+def sample_rows(M, bm, n=12, seed=0):
+    """Rows spread over row-blocks: first and last row of a few blocks plus random ones."""
+    rng = np.random.default_rng(seed)
+    nrb = M // bm
+    blocks = sorted(set([0, nrb - 1] + list(rng.integers(0, nrb, 3))))
+    rows = set()
+    for b in blocks:
+        rows.update([b * bm, b * bm + bm - 1])
+    rows.update(rng.integers(0, M, max(0, n - len(rows))).tolist())
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+@pytest.mark.parametrize("key", ["c3", "c4", "c5"])
+def test_full_size_sampled_parity(rt, key):
+    """Full-size run in the benchmark's launch configuration; the oracle
+    computes sampled rows one by one (rows of a chain are independent)."""
+    cfg = gen.CONFIGS[key]
+    tile = tuning.TILES[key]
+    say(key, "generating inputs")
+    X, Ws = gen.config_inputs(cfg)
+    say(key, "running tile", tile)
+    out, st = run_modes(rt, X, Ws, cfg.dtype, tile, acts=list(cfg.acts), flags=rt_flags()["DEBUG"],
+                        modes=("pipelined", "sequential"))
+    rows = sample_rows(cfg.M, tile[0])
+    say(key, "oracle rows", rows.tolist())
+    ref = oracle.chain(X, Ws, cfg.dtype, acts=list(cfg.acts), rows=rows)
+    err = oracle.rel_err(as_values(out["pipelined"][rows], cfg.dtype), ref)
+    say(key, "sampled rel err", err, "stats", st)
+    assert err <= TOL[gen.BF16]
+    assert same_bits(out["pipelined"], out["sequential"])
+    assert np.all(np.isfinite(as_values(out["pipelined"], cfg.dtype)))

@@ -1,0 +1,173 @@
+"""Host-side tests of the C-ABI library (no GPU needed): the library loads
+and exports every symbol include/cp_chain.h declares, the dependency-table
+builder matches the hand-derived golden graph and the structural rule of the
+chain, and argument errors map to the documented codes."""
+import os
+import re
+
+import pytest
+
+from tile_dependency_pipelined_amd import inputs as gen
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cp_chain.h")
+
+nat = pytest.importorskip("tile_dependency_pipelined_amd.native",
+                          reason="libcpchain.so not built (python -m tile_dependency_pipelined_amd.build)")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(cp_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_symbols_exported():
+    names = header_functions()
+    assert set(names) == set(nat.EXPORTS), names
+    for n in names:
+        assert hasattr(nat.lib(), n), n  # resolves through dlsym
+
+
+def test_header_constants_match_binding():
+    src = open(HEADER).read()
+    for name in ("CP_F32", "CP_BF16", "CP_ACT_NONE", "CP_ACT_GELU_TANH", "CP_MODE_PIPELINED",
+                 "CP_MODE_SEQUENTIAL", "CP_MODE_MICROBATCH", "CP_OK", "CP_ERR_INVALID_ARG",
+                 "CP_ERR_SHAPE", "CP_ERR_UNSUPPORTED", "CP_ERR_OOM", "CP_ERR_HIP", "CP_ERR_TIMEOUT",
+                 "CP_ERR_NO_DEVICE", "CP_ERR_INVARIANT", "CP_MAX_LAYERS"):
+        m = re.search(rf"#define\s+{name}\s+\(?(-?\d+)\)?", src)
+        assert m, name
+        assert int(m.group(1)) == getattr(nat, name), name
+    for name in ("CP_FLAG_DEBUG", "CP_FLAG_TRACE", "CP_FLAG_POISON", "CP_FLAG_DELAY_INJECT",
+                 "CP_FLAG_STARVE_LAST"):
+        m = re.search(rf"#define\s+{name}\s+(\d+)u", src)
+        assert m and int(m.group(1)) == getattr(nat, name), name
+
+
+def read_golden(path):
+    out = {"edges": {}}
+    for line in open(path):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        parts = line.split()
+        if parts[0] in ("n_tiles", "n_first", "n_edges"):
+            out[parts[0]] = int(parts[1])
+        elif parts[0] == "layer_off":
+            out["layer_off"] = [int(x) for x in parts[1:]]
+        else:
+            out["edges"][int(parts[0])] = [int(x) for x in parts[1:]]
+    return out
+
+
+def test_tile_graph_matches_hand_derived_golden():
+    gold = read_golden(os.path.join(ROOT, "tests", "golden", "c1_tile_graph.txt"))
+    g = nat.cp_chain_tile_graph(128, [512, 512, 512], 64, 64)
+    assert g["n_tiles"] == gold["n_tiles"]
+    assert g["n_edges"] == gold["n_edges"]
+    assert g["layer_off"] == gold["layer_off"]
+    assert g["layer_off"][1] == gold["n_first"]
+    for p, cons in gold["edges"].items():
+        assert g["dep_ids"][g["dep_off"][p]:g["dep_off"][p + 1]] == cons
+    assert g["indeg"] == [0] * 16 + [8] * 16
+
+
+def check_graph_rule(M, widths, bm, bn):
+    g = nat.cp_chain_tile_graph(M, widths, bm, bn)
+    L = len(widths) - 1
+    nrb = M // bm
+    nbn = [w // bn for w in widths[1:]]
+    off = [0]
+    for l in range(L):
+        off.append(off[-1] + nrb * nbn[l])
+    assert g["layer_off"] == off
+    T = off[-1]
+    assert g["n_tiles"] == T
+    edges = set()
+    for p in range(T):
+        for c in g["dep_ids"][g["dep_off"][p]:g["dep_off"][p + 1]]:
+            assert (p, c) not in edges
+            edges.add((p, c))
+    # expected edge set from the rule: (l, i, k) -> (l+1, i, j) for all k, j
+    want = set()
+    for l in range(L - 1):
+        for i in range(nrb):
+            for k in range(nbn[l]):
+                for j in range(nbn[l + 1]):
+                    want.add((off[l] + i * nbn[l] + k, off[l + 1] + i * nbn[l + 1] + j))
+    assert edges == want
+    assert g["n_edges"] == len(want)
+    indeg = [0] * T
+    for _, c in edges:
+        indeg[c] += 1
+    assert g["indeg"] == indeg
+    return g
+
+
+@pytest.mark.parametrize("M,widths,bm,bn", [
+    (128, [512, 512, 512], 64, 64),
+    (512, [4096, 4096, 4096], 128, 128),
+    (256, [64, 192, 128, 320], 64, 64),
+    (64, [64, 64], 64, 64),
+    (256, [128] * 9, 128, 64),
+])
+def test_tile_graph_rule(M, widths, bm, bn):
+    check_graph_rule(M, widths, bm, bn)
+
+
+@pytest.mark.parametrize("key,bm,bn,T,E,indeg", [
+    ("c2", 256, 256, 64, 512, 16), ("c2", 128, 128, 256, 4096, 32),
+    ("c3", 256, 256, 512, 8192, 32), ("c3", 128, 128, 2048, 65536, 64),
+    ("c4", 256, 256, 512, 12288, 32), ("c4", 128, 128, 2048, 98304, 64),
+    ("c5", 256, 256, 144, 3584, 112), ("c5", 64, 256, 576, 14336, 112),
+])
+def test_tile_graph_counts_for_workloads(key, bm, bn, T, E, indeg):
+    cfg = gen.CONFIGS[key]
+    g = nat.cp_chain_tile_graph(cfg.M, list(cfg.widths), bm, bn)
+    assert (g["n_tiles"], g["n_edges"]) == (T, E)
+    assert max(g["indeg"]) == indeg
+
+
+def test_error_codes_without_device():
+    with pytest.raises(nat.CpError) as e:
+        nat.cp_chain_tile_graph(100, [512, 512], 64, 64)
+    assert e.value.code == nat.CP_ERR_SHAPE
+    with pytest.raises(nat.CpError) as e:
+        nat.cp_chain_tile_graph(128, [512, 500], 64, 64)
+    assert e.value.code == nat.CP_ERR_SHAPE
+    with pytest.raises(nat.CpError) as e:
+        nat.cp_chain_tile_graph(128, [512] * 10, 64, 64)
+    assert e.value.code == nat.CP_ERR_INVALID_ARG
+    # unsupported tile is rejected before any device work
+    with pytest.raises(nat.CpError) as e:
+        nat.cp_chain_plan(128, [512, 512], nat.CP_BF16, 96, 64)
+    assert e.value.code == nat.CP_ERR_UNSUPPORTED
+    with pytest.raises(nat.CpError) as e:
+        nat.cp_chain_plan(128, [512, 512], nat.CP_F32, 128, 128)
+    assert e.value.code == nat.CP_ERR_UNSUPPORTED
+    # k not a multiple of the k step
+    with pytest.raises(nat.CpError) as e:
+        nat.cp_chain_plan(128, [96, 512], nat.CP_BF16, 64, 64)
+    assert e.value.code == nat.CP_ERR_SHAPE
+    with pytest.raises(nat.CpError) as e:
+        nat.cp_chain_plan(128, [512, 512], 7, 64, 64)
+    assert e.value.code == nat.CP_ERR_INVALID_ARG
+    with pytest.raises(nat.CpError) as e:
+        nat.cp_chain_plan(128, [512, 512], nat.CP_BF16, 64, 64, flags=1 << 12)
+    assert e.value.code == nat.CP_ERR_INVALID_ARG
+    assert nat.error_string(nat.CP_ERR_TIMEOUT)
+    assert nat.error_string(12345) == "unknown status"
+
+
+def test_plan_without_device_reports_no_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is visible")
+    with pytest.raises(nat.CpError) as e:
+        nat.cp_chain_plan(128, [512, 512, 512], nat.CP_F32, 64, 64)
+    assert e.value.code == nat.CP_ERR_NO_DEVICE
+
+
+def test_destroy_null_is_noop():
+    assert nat.lib().cp_chain_destroy(None) == 0
+    assert nat.lib().cp_chain_run(None, None, None, None, None, 0, 0) == nat.CP_ERR_INVALID_ARG

@@ -1,0 +1,472 @@
+// cp_chain.cpp -- host side of the C ABI declared in include/cp_chain.h:
+// argument validation, the dependency-table builder, plan-owned device state,
+// the three execution modes, and the invariant read-back.
+//
+// Method: CTA-Pipelining (arXiv 2607.07862).  The dependency structure --
+// dependency arrays, scoreboards and work-queues (§III-A) -- is built here
+// from the static tile dataflow of the GEMM chain: in the two-layer running
+// example (§III-B) a tile (i, j) of the second GEMM reads row-block i of the
+// first GEMM's output across all its columns, so it depends on every tile
+// (i, k) of that row-block.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "cp_chain.h"
+#include "cp_device.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+#define CP_HIP(call)                                                                     \
+    do {                                                                                 \
+        hipError_t e_ = (call);                                                          \
+        if (e_ != hipSuccess)                                                            \
+            return fail(e_ == hipErrorOutOfMemory ? CP_ERR_OOM : CP_ERR_HIP, "%s: %s (%s:%d)", \
+                        #call, hipGetErrorString(e_), __FILE__, __LINE__);               \
+    } while (0)
+
+// Tile graph of a chain: flat IDs, in-degree template and CSR out-edges.
+struct TileGraph {
+    int32_t T = 0, P1 = 0, E = 0;
+    std::vector<int32_t> layer_off, nbn, indeg, dep_off, dep_ids;
+};
+
+int check_shape(int64_t M, int32_t L, const int64_t *widths, int32_t tile_m, int32_t tile_n,
+                int32_t k_step) {
+    if (L < 1 || L > CP_MAX_LAYERS) return fail(CP_ERR_INVALID_ARG, "n_layers %d not in [1, %d]", L, CP_MAX_LAYERS);
+    if (!widths) return fail(CP_ERR_INVALID_ARG, "widths is NULL");
+    if (tile_m <= 0 || tile_n <= 0) return fail(CP_ERR_INVALID_ARG, "tile %dx%d", tile_m, tile_n);
+    if (M <= 0) return fail(CP_ERR_SHAPE, "M = %lld must be positive", (long long)M);
+    if (M % tile_m) return fail(CP_ERR_SHAPE, "M = %lld is not a multiple of tile_m = %d", (long long)M, tile_m);
+    int64_t tiles = 0;
+    for (int l = 0; l <= L; ++l) {
+        if (widths[l] <= 0) return fail(CP_ERR_SHAPE, "widths[%d] = %lld must be positive", l, (long long)widths[l]);
+        if (widths[l] > (int64_t)1 << 30) return fail(CP_ERR_SHAPE, "widths[%d] too large", l);
+        if (l < L && k_step > 0 && widths[l] % k_step)
+            return fail(CP_ERR_SHAPE, "contraction length widths[%d] = %lld is not a multiple of %d", l,
+                        (long long)widths[l], k_step);
+        if (l > 0) {
+            if (widths[l] % tile_n)
+                return fail(CP_ERR_SHAPE, "N_%d = %lld is not a multiple of tile_n = %d", l, (long long)widths[l], tile_n);
+            tiles += (M / tile_m) * (widths[l] / tile_n);
+        }
+    }
+    if (M > (int64_t)1 << 30) return fail(CP_ERR_SHAPE, "M too large");
+    if (tiles >= (int64_t)0x7FFFFFF0) return fail(CP_ERR_SHAPE, "too many tiles");
+    return CP_OK;
+}
+
+// Dependency table (§III-A): tile (l+1, i, j) waits on all N_l / tile_n tiles
+// (l, i, k) of row-block i, because its A operand is that whole row-block.
+void build_graph(int64_t M, int32_t L, const int64_t *widths, int32_t tile_m, int32_t tile_n,
+                 TileGraph &g) {
+    const int32_t nrb = (int32_t)(M / tile_m);
+    g.layer_off.assign(L + 1, 0);
+    g.nbn.assign(L, 0);
+    for (int l = 0; l < L; ++l) {
+        g.nbn[l] = (int32_t)(widths[l + 1] / tile_n);
+        g.layer_off[l + 1] = g.layer_off[l] + nrb * g.nbn[l];
+    }
+    g.T = g.layer_off[L];
+    g.P1 = g.layer_off[1];
+    g.indeg.assign(g.T, 0);
+    g.dep_off.assign(g.T + 1, 0);
+    for (int l = 0; l < L; ++l)
+        for (int32_t t = g.layer_off[l]; t < g.layer_off[l + 1]; ++t) {
+            if (l > 0) g.indeg[t] = g.nbn[l - 1];
+            g.dep_off[t + 1] = g.dep_off[t] + (l + 1 < L ? g.nbn[l + 1] : 0);
+        }
+    g.E = g.dep_off[g.T];
+    g.dep_ids.assign(g.E, 0);
+    for (int l = 0; l + 1 < L; ++l)
+        for (int32_t i = 0; i < nrb; ++i)
+            for (int32_t k = 0; k < g.nbn[l]; ++k) {
+                const int32_t p = g.layer_off[l] + i * g.nbn[l] + k;
+                int32_t e = g.dep_off[p];
+                for (int32_t j = 0; j < g.nbn[l + 1]; ++j)
+                    g.dep_ids[e++] = g.layer_off[l + 1] + i * g.nbn[l + 1] + j;
+            }
+}
+
+}  // namespace
+
+struct cp_chain {
+    int64_t M = 0;
+    int32_t L = 0;
+    int64_t widths[CP_MAX_LAYERS + 1] = {};
+    int32_t dtype = 0, tile_m = 0, tile_n = 0;
+    int32_t acts[CP_MAX_LAYERS] = {};
+    uint32_t flags = 0;
+    int device = 0;
+    const cp::Variant *var = nullptr;
+    TileGraph g;
+    int n_workers = 0;
+    // device state (one allocation) and intermediates
+    char *state = nullptr;
+    int32_t *d_score = nullptr, *d_indeg = nullptr, *d_dep_off = nullptr, *d_dep_ids = nullptr;
+    uint32_t *d_queue = nullptr, *d_ctl = nullptr, *d_deq = nullptr;
+    uint64_t *d_trace = nullptr;
+    void *inter[CP_MAX_LAYERS] = {};
+    size_t inter_bytes[CP_MAX_LAYERS] = {};
+    hipStream_t side[2] = {nullptr, nullptr};
+    hipEvent_t ev_fork = nullptr, ev_join[2] = {nullptr, nullptr};
+    hipEvent_t ev_start = nullptr, ev_kernel = nullptr, ev_stop = nullptr;
+    uint64_t timeout_ticks = 200000000ull;  // 2 s at 100 MHz
+    int32_t last_mode = -1;
+    bool ran = false;
+};
+
+namespace {
+
+void release(cp_chain *p) {
+    if (!p) return;
+    for (auto &s : p->side)
+        if (s) (void)hipStreamDestroy(s);
+    if (p->ev_fork) (void)hipEventDestroy(p->ev_fork);
+    for (auto &e : p->ev_join)
+        if (e) (void)hipEventDestroy(e);
+    if (p->ev_start) (void)hipEventDestroy(p->ev_start);
+    if (p->ev_kernel) (void)hipEventDestroy(p->ev_kernel);
+    if (p->ev_stop) (void)hipEventDestroy(p->ev_stop);
+    for (auto &b : p->inter)
+        if (b) (void)hipFree(b);
+    if (p->state) (void)hipFree(p->state);
+    delete p;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+cp::ChainArgs make_args(const cp_chain *p, const void *X, const void *const *W, void *Y) {
+    cp::ChainArgs a;
+    memset(&a, 0, sizeof a);
+    const size_t es = p->dtype == CP_BF16 ? 2 : 4;
+    (void)es;
+    for (int l = 0; l < p->L; ++l) {
+        cp::LayerDesc &d = a.layer[l];
+        d.A = l == 0 ? X : p->inter[l - 1];
+        d.W = W[l];
+        d.C = l + 1 == p->L ? Y : p->inter[l];
+        d.K = (int32_t)p->widths[l];
+        d.N = (int32_t)p->widths[l + 1];
+        d.nbn = p->g.nbn[l];
+        d.act = p->acts[l];
+        d.tile_off = p->g.layer_off[l];
+        d.ntiles = p->g.layer_off[l + 1] - p->g.layer_off[l];
+    }
+    a.L = p->L;
+    a.T = p->g.T;
+    a.flags = p->flags;
+    a.queue = p->d_queue;
+    a.ctl = p->d_ctl;
+    a.score = p->d_score;
+    a.dep_off = p->d_dep_off;
+    a.dep_ids = p->d_dep_ids;
+    a.indeg = p->d_indeg;
+    a.deq_count = (p->flags & CP_FLAG_DEBUG) ? p->d_deq : nullptr;
+    a.trace = (p->flags & CP_FLAG_TRACE) ? p->d_trace : nullptr;
+    a.timeout_ticks = p->timeout_ticks;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *cp_chain_error_string(int code) {
+    switch (code) {
+        case CP_OK: return "ok";
+        case CP_ERR_INVALID_ARG: return "invalid argument";
+        case CP_ERR_SHAPE: return "shape not supported (not a multiple of the tile or k step)";
+        case CP_ERR_UNSUPPORTED: return "unsupported dtype / tile combination";
+        case CP_ERR_OOM: return "out of device memory";
+        case CP_ERR_HIP: return "HIP runtime error";
+        case CP_ERR_TIMEOUT: return "a queue wait exceeded the watchdog (dependency never satisfied)";
+        case CP_ERR_NO_DEVICE: return "no HIP device available";
+        case CP_ERR_INVARIANT: return "scoreboard / queue invariant violated";
+        default: return "unknown status";
+    }
+}
+
+const char *cp_chain_last_error(void) { return g_last_error.c_str(); }
+
+int cp_chain_tile_graph(int64_t M, int32_t n_layers, const int64_t *widths, int32_t tile_m,
+                        int32_t tile_n, int32_t *n_tiles, int32_t *n_edges, int32_t *layer_off,
+                        int32_t *indeg, int32_t *dep_off, int32_t *dep_ids) {
+    g_last_error.clear();
+    int rc = check_shape(M, n_layers, widths, tile_m, tile_n, 0);
+    if (rc) return rc;
+    TileGraph g;
+    try {
+        build_graph(M, n_layers, widths, tile_m, tile_n, g);
+    } catch (const std::bad_alloc &) {
+        return fail(CP_ERR_OOM, "host allocation failed");
+    }
+    if (n_tiles) *n_tiles = g.T;
+    if (n_edges) *n_edges = g.E;
+    if (layer_off) std::copy(g.layer_off.begin(), g.layer_off.end(), layer_off);
+    if (indeg) std::copy(g.indeg.begin(), g.indeg.end(), indeg);
+    if (dep_off) std::copy(g.dep_off.begin(), g.dep_off.end(), dep_off);
+    if (dep_ids) std::copy(g.dep_ids.begin(), g.dep_ids.end(), dep_ids);
+    return CP_OK;
+}
+
+int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *widths,
+                  int32_t dtype, int32_t tile_m, int32_t tile_n, const int32_t *acts,
+                  uint32_t flags) {
+    g_last_error.clear();
+    if (!out) return fail(CP_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (dtype != CP_F32 && dtype != CP_BF16) return fail(CP_ERR_INVALID_ARG, "dtype %d", dtype);
+    const cp::Variant *var = cp::find_variant(dtype, tile_m, tile_n);
+    if (!var)
+        return fail(CP_ERR_UNSUPPORTED, "no %s kernel for tile %dx%d", dtype == CP_BF16 ? "bf16" : "fp32",
+                    tile_m, tile_n);
+    int rc = check_shape(M, n_layers, widths, tile_m, tile_n, var->k_step);
+    if (rc) return rc;
+    if (acts)
+        for (int l = 0; l < n_layers; ++l)
+            if (acts[l] != CP_ACT_NONE && acts[l] != CP_ACT_GELU_TANH)
+                return fail(CP_ERR_INVALID_ARG, "acts[%d] = %d", l, acts[l]);
+    const uint32_t known = CP_FLAG_DEBUG | CP_FLAG_TRACE | CP_FLAG_POISON | CP_FLAG_DELAY_INJECT | CP_FLAG_STARVE_LAST;
+    if (flags & ~known) return fail(CP_ERR_INVALID_ARG, "unknown flags 0x%x", flags & ~known);
+    if ((flags & CP_FLAG_STARVE_LAST) && n_layers < 2)
+        return fail(CP_ERR_INVALID_ARG, "CP_FLAG_STARVE_LAST needs at least two layers");
+
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0)
+        return fail(CP_ERR_NO_DEVICE, "no HIP device visible");
+
+    cp_chain *p = new (std::nothrow) cp_chain();
+    if (!p) return fail(CP_ERR_OOM, "host allocation failed");
+    p->M = M;
+    p->L = n_layers;
+    for (int l = 0; l <= n_layers; ++l) p->widths[l] = widths[l];
+    p->dtype = dtype;
+    p->tile_m = tile_m;
+    p->tile_n = tile_n;
+    for (int l = 0; l < n_layers; ++l) p->acts[l] = acts ? acts[l] : CP_ACT_NONE;
+    p->flags = flags;
+    p->var = var;
+    auto bail = [&](int code) {
+        release(p);
+        return code;
+    };
+    if (hipGetDevice(&p->device) != hipSuccess) return bail(fail(CP_ERR_NO_DEVICE, "hipGetDevice failed"));
+    try {
+        build_graph(M, n_layers, widths, tile_m, tile_n, p->g);
+    } catch (const std::bad_alloc &) {
+        return bail(fail(CP_ERR_OOM, "host allocation failed"));
+    }
+    if (flags & CP_FLAG_STARVE_LAST) p->g.indeg[p->g.T - 1] += 1;
+    const TileGraph &g = p->g;
+
+    // one device allocation for all protocol state
+    const size_t T = (size_t)g.T, E = (size_t)std::max(g.E, 1);
+    size_t off = 0;
+    const size_t o_ctl = off;     off = align_up(off + cp::kCtlWords * 4, 256);
+    const size_t o_score = off;   off = align_up(off + T * 4, 256);
+    const size_t o_queue = off;   off = align_up(off + T * 4, 256);
+    const size_t o_indeg = off;   off = align_up(off + T * 4, 256);
+    const size_t o_doff = off;    off = align_up(off + (T + 1) * 4, 256);
+    const size_t o_dids = off;    off = align_up(off + E * 4, 256);
+    const size_t o_deq = off;     off = align_up(off + T * 4, 256);
+    const size_t o_trace = off;   off = align_up(off + ((flags & CP_FLAG_TRACE) ? T * 32 : 0), 256);
+    int rc2 = [&]() -> int {
+        CP_HIP(hipMalloc(&p->state, off));
+        p->d_ctl = reinterpret_cast<uint32_t *>(p->state + o_ctl);
+        p->d_score = reinterpret_cast<int32_t *>(p->state + o_score);
+        p->d_queue = reinterpret_cast<uint32_t *>(p->state + o_queue);
+        p->d_indeg = reinterpret_cast<int32_t *>(p->state + o_indeg);
+        p->d_dep_off = reinterpret_cast<int32_t *>(p->state + o_doff);
+        p->d_dep_ids = reinterpret_cast<int32_t *>(p->state + o_dids);
+        p->d_deq = reinterpret_cast<uint32_t *>(p->state + o_deq);
+        p->d_trace = (flags & CP_FLAG_TRACE) ? reinterpret_cast<uint64_t *>(p->state + o_trace) : nullptr;
+        CP_HIP(hipMemset(p->state, 0, off));
+        CP_HIP(hipMemcpy(p->d_indeg, g.indeg.data(), T * 4, hipMemcpyHostToDevice));
+        CP_HIP(hipMemcpy(p->d_dep_off, g.dep_off.data(), (T + 1) * 4, hipMemcpyHostToDevice));
+        if (g.E) CP_HIP(hipMemcpy(p->d_dep_ids, g.dep_ids.data(), (size_t)g.E * 4, hipMemcpyHostToDevice));
+        const size_t es = dtype == CP_BF16 ? 2 : 4;
+        for (int l = 0; l + 1 < n_layers; ++l) {
+            p->inter_bytes[l] = (size_t)M * (size_t)widths[l + 1] * es;
+            CP_HIP(hipMalloc(&p->inter[l], p->inter_bytes[l]));
+        }
+        for (auto &s : p->side) CP_HIP(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
+        CP_HIP(hipEventCreateWithFlags(&p->ev_fork, hipEventDisableTiming));
+        for (auto &e : p->ev_join) CP_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+        CP_HIP(hipEventCreate(&p->ev_start));
+        CP_HIP(hipEventCreate(&p->ev_kernel));
+        CP_HIP(hipEventCreate(&p->ev_stop));
+        int per_cu = 0, cus = 0;
+        CP_HIP(var->occupancy(&per_cu));
+        CP_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device));
+        if (per_cu < 1) return fail(CP_ERR_UNSUPPORTED, "kernel cannot be resident (occupancy 0)");
+        p->n_workers = std::max(1, std::min(per_cu * cus, g.T));
+        int clk_khz = 0;
+        if (hipDeviceGetAttribute(&clk_khz, hipDeviceAttributeWallClockRate, p->device) == hipSuccess &&
+            clk_khz > 0)
+            p->timeout_ticks = (uint64_t)clk_khz * 1000ull * 2ull;  // 2 s
+        if (flags & CP_FLAG_STARVE_LAST) p->timeout_ticks = (uint64_t)std::max(clk_khz, 1) * 50ull;  // 50 ms
+        return CP_OK;
+    }();
+    if (rc2) return bail(rc2);
+    *out = p;
+    return CP_OK;
+}
+
+int cp_chain_run(cp_chain *p, const void *X, const void *const *W, void *Y, void *stream,
+                 int32_t mode, int64_t microbatch_rows) {
+    g_last_error.clear();
+    if (!p) return fail(CP_ERR_INVALID_ARG, "plan is NULL");
+    if (!X || !W || !Y) return fail(CP_ERR_INVALID_ARG, "X, W or Y is NULL");
+    for (int l = 0; l < p->L; ++l)
+        if (!W[l]) return fail(CP_ERR_INVALID_ARG, "W[%d] is NULL", l);
+    if (mode != CP_MODE_PIPELINED && mode != CP_MODE_SEQUENTIAL && mode != CP_MODE_MICROBATCH)
+        return fail(CP_ERR_INVALID_ARG, "mode %d", mode);
+    if (mode == CP_MODE_MICROBATCH) {
+        if (microbatch_rows <= 0 || microbatch_rows % p->tile_m || p->M % microbatch_rows)
+            return fail(CP_ERR_SHAPE, "microbatch_rows = %lld must be a positive multiple of tile_m = %d dividing M = %lld",
+                        (long long)microbatch_rows, p->tile_m, (long long)p->M);
+    }
+    int cur = -1;
+    CP_HIP(hipGetDevice(&cur));
+    if (cur != p->device) return fail(CP_ERR_INVALID_ARG, "current device %d differs from the plan's %d", cur, p->device);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const cp::ChainArgs a = make_args(p, X, W, Y);
+
+    CP_HIP(hipEventRecord(p->ev_start, s));
+    if (p->flags & CP_FLAG_POISON)
+        for (int l = 0; l + 1 < p->L; ++l) CP_HIP(cp::launch_poison(p->inter[l], p->inter_bytes[l], p->dtype, s));
+    if (mode == CP_MODE_PIPELINED) {
+        CP_HIP(cp::launch_reset(a, p->g.P1, s));
+        CP_HIP(hipEventRecord(p->ev_kernel, s));
+        CP_HIP(p->var->launch_worker(a, p->n_workers, s));
+    } else if (mode == CP_MODE_SEQUENTIAL) {
+        const int nrb = (int)(p->M / p->tile_m);
+        for (int l = 0; l < p->L; ++l) CP_HIP(p->var->launch_layer(a, l, 0, nrb, s));
+    } else {
+        const int chunk_rb = (int)(microbatch_rows / p->tile_m);
+        const int nchunks = (int)(p->M / microbatch_rows);
+        CP_HIP(hipEventRecord(p->ev_fork, s));
+        for (auto &side : p->side) CP_HIP(hipStreamWaitEvent(side, p->ev_fork, 0));
+        for (int c = 0; c < nchunks; ++c) {
+            hipStream_t cs = p->side[c & 1];
+            for (int l = 0; l < p->L; ++l) CP_HIP(p->var->launch_layer(a, l, c * chunk_rb, chunk_rb, cs));
+        }
+        for (int k = 0; k < 2; ++k) {
+            CP_HIP(hipEventRecord(p->ev_join[k], p->side[k]));
+            CP_HIP(hipStreamWaitEvent(s, p->ev_join[k], 0));
+        }
+    }
+    CP_HIP(hipEventRecord(p->ev_stop, s));
+    p->last_mode = mode;
+    p->ran = true;
+    return CP_OK;
+}
+
+int cp_chain_stats(cp_chain *p, cp_chain_stats_t *out) {
+    g_last_error.clear();
+    if (!p || !out) return fail(CP_ERR_INVALID_ARG, "plan or out is NULL");
+    memset(out, 0, sizeof *out);
+    out->mode = p->last_mode;
+    out->n_tiles = p->g.T;
+    out->n_first = p->g.P1;
+    out->n_edges = p->g.E;
+    out->n_workers = p->n_workers;
+    out->tile_m = p->tile_m;
+    out->tile_n = p->tile_n;
+    out->bad_dequeues = -1;
+    out->order_violations = -1;
+    if (!p->ran) return CP_OK;
+    CP_HIP(hipEventSynchronize(p->ev_stop));
+    float ms = 0.f;
+    CP_HIP(hipEventElapsedTime(&ms, p->ev_start, p->ev_stop));
+    out->last_run_ms = ms;
+    out->last_kernel_ms = ms;
+    if (p->last_mode != CP_MODE_PIPELINED) return CP_OK;
+    CP_HIP(hipEventElapsedTime(&ms, p->ev_kernel, p->ev_stop));
+    out->last_kernel_ms = ms;
+
+    const size_t T = (size_t)p->g.T;
+    uint32_t ctl[cp::kCtlWords];
+    std::vector<int32_t> score(T);
+    std::vector<uint32_t> queue(T);
+    CP_HIP(hipMemcpy(ctl, p->d_ctl, sizeof ctl, hipMemcpyDeviceToHost));
+    CP_HIP(hipMemcpy(score.data(), p->d_score, T * 4, hipMemcpyDeviceToHost));
+    CP_HIP(hipMemcpy(queue.data(), p->d_queue, T * 4, hipMemcpyDeviceToHost));
+    out->status = (int32_t)ctl[cp::kCtlStatus];
+    out->head = ctl[cp::kCtlHead];
+    out->tail = ctl[cp::kCtlTail];
+    int32_t nz = 0;
+    for (size_t t = 0; t < T; ++t) nz += score[t] != 0;
+    out->nonzero_scores = nz;
+    std::vector<uint8_t> seen(T, 0);
+    bool perm = true;
+    for (size_t t = 0; t < T; ++t) {
+        if (queue[t] >= T || seen[queue[t]]) {
+            perm = false;
+            break;
+        }
+        seen[queue[t]] = 1;
+    }
+    out->queue_is_perm = perm ? 1 : 0;
+    if (p->flags & CP_FLAG_DEBUG) {
+        std::vector<uint32_t> deq(T);
+        CP_HIP(hipMemcpy(deq.data(), p->d_deq, T * 4, hipMemcpyDeviceToHost));
+        int32_t bad = 0;
+        for (size_t t = 0; t < T; ++t) bad += deq[t] != 1;
+        out->bad_dequeues = bad;
+    }
+    if (p->flags & CP_FLAG_TRACE) {
+        std::vector<uint64_t> tr(T * 4);
+        CP_HIP(hipMemcpy(tr.data(), p->d_trace, T * 32, hipMemcpyDeviceToHost));
+        int32_t viol = 0;
+        for (size_t pr = 0; pr < T; ++pr)
+            for (int32_t e = p->g.dep_off[pr]; e < p->g.dep_off[pr + 1]; ++e) {
+                const size_t c = (size_t)p->g.dep_ids[e];
+                if (tr[4 * c + 1] < tr[4 * pr + 3]) ++viol;  // consumer dequeued before producer released
+            }
+        out->order_violations = viol;
+    }
+    if (out->status != 0) return fail(out->status, "device status %d: %s", out->status, cp_chain_error_string(out->status));
+    return CP_OK;
+}
+
+int cp_chain_trace(cp_chain *p, uint64_t *out, int64_t capacity) {
+    g_last_error.clear();
+    if (!p || !out) return fail(CP_ERR_INVALID_ARG, "plan or out is NULL");
+    if (!(p->flags & CP_FLAG_TRACE)) return fail(CP_ERR_INVALID_ARG, "plan was built without CP_FLAG_TRACE");
+    if (capacity < 4 * (int64_t)p->g.T) return fail(CP_ERR_INVALID_ARG, "capacity %lld < 4*T", (long long)capacity);
+    if (p->ran) CP_HIP(hipEventSynchronize(p->ev_stop));
+    CP_HIP(hipMemcpy(out, p->d_trace, (size_t)p->g.T * 32, hipMemcpyDeviceToHost));
+    return CP_OK;
+}
+
+int cp_chain_destroy(cp_chain *p) {
+    g_last_error.clear();
+    if (!p) return CP_OK;
+    if (p->ran) (void)hipEventSynchronize(p->ev_stop);
+    for (auto &s : p->side)
+        if (s) (void)hipStreamSynchronize(s);
+    release(p);
+    return CP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,514 @@
+// cp_kernels.hip -- device code of the tile-pipelined GEMM chain for gfx950.
+//
+// Method: CTA-Pipelining: A Latency-Oriented Spatial Scaling Method for
+// Multi-GPU Systems (arXiv 2607.07862).  A workgroup plays the role of the
+// paper's CTA: it consumes input tiles and produces exactly one output tile
+// (§III, execution model).  The GEMM tile body is left unchanged; only a
+// prologue (take a queue slot, wait until it holds a ready tile ID, remap the
+// workgroup to that tile) and an epilogue (store, release, decrement the
+// scoreboard of every consumer, push consumers that became ready) are added
+// around it (§III-A "dependency structure"; §III-C; Fig. 2).  The same body is
+// launched without prologue/epilogue for the sequential and micro-batched
+// baselines, so all modes produce bit-identical results.
+//
+// gfx950 mapping (MI355X): 256 threads = 4 wave64 per workgroup; bf16 tiles
+// use v_mfma_f32_32x32x16_bf16 with fp32 accumulators, fp32 tiles use
+// v_mfma_f32_32x32x2_f32; operands are staged HBM -> VGPR -> LDS with 128-bit
+// loads and double-buffered LDS; the paper's system-wide threadfence becomes
+// an agent-scope release (L2 write-back, the L2 being private to each XCD)
+// and the consumer's read of the scoreboard an agent-scope acquire.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "cp_chain.h"
+#include "cp_device.h"
+
+namespace cp {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// ----------------------------------------------------------------------------
+// Element conversion and activation (applied to the fp32 accumulator).
+// ----------------------------------------------------------------------------
+
+// fp32 -> bf16, round to nearest even (inputs here are finite; NaN is kept NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ float act_apply(float x, int act) {
+    if (act == CP_ACT_GELU_TANH) {
+        // x/2 (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))
+        const float k0 = 0.7978845608028654f;
+        float u = k0 * (x + 0.044715f * x * x * x);
+        return 0.5f * x * (1.0f + tanhf(u));
+    }
+    return x;
+}
+
+// ----------------------------------------------------------------------------
+// bf16 tile body: C[BM x BN] tile (i, j) of A[M][K] . W[K][N], BK = 64.
+//
+// LDS holds both operands "k-contiguous": A as [BM][64] and W transposed to
+// [BN][64], 128 bytes per row, in 16-byte chunks XOR-swizzled by
+// sw(r) = (r ^ (r >> 3)) & 7 so that the fragment reads (8 consecutive rows,
+// same chunk), the A stores (one row, 8 chunks) and the transposed W stores
+// (rows 8 apart) all touch 32 distinct banks.
+// W is row-major [K][N] (n contiguous): each thread loads BN/32 rows of one
+// 16-byte column chunk and transposes that (BN/32) x 8 block in registers.
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ int sw(int r) { return (r ^ (r >> 3)) & 7; }
+
+template <int BM_, int BN_>
+struct Bf16Body {
+    static constexpr int BM = BM_, BN = BN_, BK = 64;
+    static constexpr int WM = BM / 2, WN = BN / 2;   // per-wave sub-tile (2 x 2 waves)
+    static constexpr int FM = WM / 32, FN = WN / 32; // 32x32 MFMA blocks per wave
+    static constexpr int A_LD = BM * 8 / kThreads;  // 16-byte A loads per thread
+    static constexpr int NCH = BN / 8;               // 16-byte chunks per W row
+    static constexpr int KR = BK * NCH / kThreads;   // W rows per thread (= BN/32)
+    static constexpr int STAGE = (BM + BN) * BK * 2; // bytes per LDS stage
+    static constexpr int LDS = 2 * STAGE;
+    static_assert(BM >= 64 && BN >= 64 && BM <= 256 && BN <= 256, "tile");
+    static_assert(KR >= 2 && KR <= 8 && (KR & 1) == 0, "W rows per thread");
+
+    __device__ static void run(const LayerDesc &d, int i, int j, char *lds) {
+        const uint16_t *__restrict__ A = static_cast<const uint16_t *>(d.A);
+        const uint16_t *__restrict__ W = static_cast<const uint16_t *>(d.W);
+        uint16_t *__restrict__ C = static_cast<uint16_t *>(d.C);
+        const int K = d.K, N = d.N;
+        const int row0 = i * BM, col0 = j * BN;
+        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+        const int wm = wave >> 1, wn = wave & 1;
+
+        f32x16_t acc[FM][FN];
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.0f;
+
+        // global addressing
+        const uint16_t *a_src = A + (size_t)(row0 + (tid >> 3)) * K + (tid & 7) * 8;
+        const int b_nch = tid % NCH, b_kg = tid / NCH;
+        const uint16_t *b_src = W + (size_t)(b_kg * KR) * N + col0 + b_nch * 8;
+
+        uint4 ra[A_LD], rb[KR];
+        auto gload = [&](int k0) {
+#pragma unroll
+            for (int q = 0; q < A_LD; ++q)
+                ra[q] = *reinterpret_cast<const uint4 *>(a_src + (size_t)q * 32 * K + k0);
+#pragma unroll
+            for (int kk = 0; kk < KR; ++kk)
+                rb[kk] = *reinterpret_cast<const uint4 *>(b_src + (size_t)(k0 + kk) * N);
+        };
+        auto lstore = [&](int buf) {
+            char *As = lds + buf * STAGE;
+            char *Bs = As + BM * BK * 2;
+#pragma unroll
+            for (int q = 0; q < A_LD; ++q) {
+                const int r = q * 32 + (tid >> 3);
+                *reinterpret_cast<uint4 *>(As + r * 128 + (((tid & 7) ^ sw(r)) << 4)) = ra[q];
+            }
+            const int kb = b_kg * KR;  // first k of this thread's rows within the slab
+            const int lch = kb >> 3, within = (kb & 7) * 2;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int n = b_nch * 8 + e;
+                char *dst = Bs + n * 128 + ((lch ^ sw(n)) << 4) + within;
+                uint32_t w[KR / 2];
+#pragma unroll
+                for (int p = 0; p < KR / 2; ++p) {
+                    const uint32_t lo = reinterpret_cast<const uint32_t *>(&rb[2 * p])[e >> 1];
+                    const uint32_t hi = reinterpret_cast<const uint32_t *>(&rb[2 * p + 1])[e >> 1];
+                    w[p] = (e & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
+                }
+                if constexpr (KR == 8) {
+                    *reinterpret_cast<uint4 *>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+                } else if constexpr (KR == 4) {
+                    *reinterpret_cast<uint2 *>(dst) = make_uint2(w[0], w[1]);
+                } else {
+                    *reinterpret_cast<uint32_t *>(dst) = w[0];
+                }
+            }
+        };
+        auto compute = [&](int buf) {
+            const char *As = lds + buf * STAGE;
+            const char *Bs = As + BM * BK * 2;
+#pragma unroll
+            for (int kk = 0; kk < BK / 16; ++kk) {
+                const int c = kk * 2 + (lane >> 5);
+                bf16x8_t af[FM], bfv[FN];
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm) {
+                    const int r = wm * WM + fm * 32 + (lane & 31);
+                    af[fm] = *reinterpret_cast<const bf16x8_t *>(As + r * 128 + ((c ^ sw(r)) << 4));
+                }
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) {
+                    const int n = wn * WN + fn * 32 + (lane & 31);
+                    bfv[fn] = *reinterpret_cast<const bf16x8_t *>(Bs + n * 128 + ((c ^ sw(n)) << 4));
+                }
+                // W fragment as the first operand: the result holds, per lane,
+                // output row m = lane%32 and four consecutive output columns.
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn)
+                        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfv[fn], af[fm],
+                                                                              acc[fm][fn], 0, 0, 0);
+            }
+        };
+
+        const int nk = K / BK;
+        gload(0);
+        lstore(0);
+        __syncthreads();
+        for (int ks = 0; ks < nk; ++ks) {
+            if (ks + 1 < nk) gload((ks + 1) * BK);
+            compute(ks & 1);
+            if (ks + 1 < nk) lstore((ks + 1) & 1);
+            __syncthreads();
+        }
+
+        // epilogue: activation on the fp32 accumulator, RNE to bf16, 8-byte stores
+        const int act = d.act;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int m = row0 + wm * WM + fm * 32 + (lane & 31);
+            uint16_t *crow = C + (size_t)m * N + col0 + wn * WN;
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int n = fn * 32 + g * 8 + (lane >> 5) * 4;
+                    const f32x16_t &v = acc[fm][fn];
+                    const uint32_t b0 = f32_to_bf16_rne(act_apply(v[4 * g + 0], act));
+                    const uint32_t b1 = f32_to_bf16_rne(act_apply(v[4 * g + 1], act));
+                    const uint32_t b2 = f32_to_bf16_rne(act_apply(v[4 * g + 2], act));
+                    const uint32_t b3 = f32_to_bf16_rne(act_apply(v[4 * g + 3], act));
+                    *reinterpret_cast<uint2 *>(crow + n) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+                }
+        }
+    }
+};
+
+// ----------------------------------------------------------------------------
+// fp32 tile body (64 x 64, BK = 32) on v_mfma_f32_32x32x2_f32.  Small chains
+// only; A is transposed into LDS ([k][m], padded) so that both fragment reads
+// are lane-contiguous.
+// ----------------------------------------------------------------------------
+struct F32Body {
+    static constexpr int BM = 64, BN = 64, BK = 32;
+    static constexpr int AP = BM + 1;  // padded A row ([k][m])
+    static constexpr int BP = BN + 4;  // padded W row ([k][n]), keeps 16-byte alignment
+    static constexpr int STAGE = (BK * AP + BK * BP) * 4;
+    static constexpr int LDS = 2 * STAGE;
+
+    __device__ static void run(const LayerDesc &d, int i, int j, char *lds) {
+        const float *__restrict__ A = static_cast<const float *>(d.A);
+        const float *__restrict__ W = static_cast<const float *>(d.W);
+        float *__restrict__ C = static_cast<float *>(d.C);
+        const int K = d.K, N = d.N;
+        const int row0 = i * BM, col0 = j * BN;
+        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+        const int wm = wave >> 1, wn = wave & 1;
+
+        f32x16_t acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+
+        float4 ra[2], rb[2];
+        auto gload = [&](int k0) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int r = q * 32 + (tid >> 3), c4 = tid & 7;
+                ra[q] = *reinterpret_cast<const float4 *>(A + (size_t)(row0 + r) * K + k0 + c4 * 4);
+                const int k = q * 16 + (tid >> 4), n4 = tid & 15;
+                rb[q] = *reinterpret_cast<const float4 *>(W + (size_t)(k0 + k) * N + col0 + n4 * 4);
+            }
+        };
+        auto lstore = [&](int buf) {
+            float *As = reinterpret_cast<float *>(lds + buf * STAGE);
+            float *Bs = As + BK * AP;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int r = q * 32 + (tid >> 3), c4 = tid & 7;
+                As[(c4 * 4 + 0) * AP + r] = ra[q].x;
+                As[(c4 * 4 + 1) * AP + r] = ra[q].y;
+                As[(c4 * 4 + 2) * AP + r] = ra[q].z;
+                As[(c4 * 4 + 3) * AP + r] = ra[q].w;
+                const int k = q * 16 + (tid >> 4), n4 = tid & 15;
+                *reinterpret_cast<float4 *>(Bs + k * BP + n4 * 4) = rb[q];
+            }
+        };
+        auto compute = [&](int buf) {
+            const float *As = reinterpret_cast<const float *>(lds + buf * STAGE);
+            const float *Bs = As + BK * AP;
+#pragma unroll
+            for (int kk = 0; kk < BK / 2; ++kk) {
+                const int k = kk * 2 + (lane >> 5);
+                const float a = As[k * AP + wm * 32 + (lane & 31)];
+                const float b = Bs[k * BP + wn * 32 + (lane & 31)];
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(b, a, acc, 0, 0, 0);
+            }
+        };
+
+        const int nk = K / BK;
+        gload(0);
+        lstore(0);
+        __syncthreads();
+        for (int ks = 0; ks < nk; ++ks) {
+            if (ks + 1 < nk) gload((ks + 1) * BK);
+            compute(ks & 1);
+            if (ks + 1 < nk) lstore((ks + 1) & 1);
+            __syncthreads();
+        }
+
+        const int act = d.act;
+        const int m = row0 + wm * 32 + (lane & 31);
+        float *crow = C + (size_t)m * N + col0 + wn * 32;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int n = g * 8 + (lane >> 5) * 4;
+            *reinterpret_cast<float4 *>(crow + n) =
+                make_float4(act_apply(acc[4 * g + 0], act), act_apply(acc[4 * g + 1], act),
+                            act_apply(acc[4 * g + 2], act), act_apply(acc[4 * g + 3], act));
+        }
+    }
+};
+
+// ----------------------------------------------------------------------------
+// Protocol: prologue (consumer side) and publish (producer side).
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t ld_relaxed(const uint32_t *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Thread 0 only.  Take the next queue slot (ticket), wait until a tile ID has
+// been pushed into it, and make the producers' stores of that tile's inputs
+// visible.  Returns the tile ID, or kDone when the queue is exhausted or the
+// run has failed.  Slots are handed out in order, so a waiting worker only
+// ever waits on tiles held by workers that took earlier slots and are
+// already running: the wait always ends for a well-formed dependency table.
+__device__ uint32_t prologue(const ChainArgs &a) {
+    if (ld_relaxed(a.ctl + kCtlStatus) != 0) return kDone;
+    const uint32_t t = __hip_atomic_fetch_add(a.ctl + kCtlHead, 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    if (t >= (uint32_t)a.T) return kDone;
+    const uint64_t t0 = wall_clock64();
+    uint32_t id;
+    uint32_t polls = 0;
+    while ((id = ld_relaxed(a.queue + t)) == kEmpty) {
+        __builtin_amdgcn_s_sleep(1);
+        if ((++polls & 63) == 0) {
+            if (wall_clock64() - t0 > a.timeout_ticks) {
+                __hip_atomic_store(a.ctl + kCtlStatus, (uint32_t)kStatusTimeout, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                return kDone;
+            }
+            if (ld_relaxed(a.ctl + kCtlStatus) != 0) return kDone;
+        }
+    }
+    if (id >= (uint32_t)a.layer[0].ntiles) {
+        // Every producer of `id` released its stores before decrementing
+        // score[id]; acquiring the final value (0) of that counter orders this
+        // workgroup's subsequent loads after all of those stores.
+        (void)__hip_atomic_load(a.score + id, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (a.deq_count)
+        __hip_atomic_fetch_add(a.deq_count + id, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (a.trace) {
+        a.trace[4 * (size_t)id + 0] = t0;
+        a.trace[4 * (size_t)id + 1] = wall_clock64();
+    }
+    return id;
+}
+
+// All threads.  Called after the tile's stores.  Each wave releases its own
+// stores at agent scope (write-back of this XCD's L2) before the barrier; then
+// wave 0 decrements the counter of every consumer, one edge per lane, and
+// pushes the consumers whose counter reached zero with one atomic on the tail.
+__device__ void publish(const ChainArgs &a, uint32_t id) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    const int tid = threadIdx.x;
+    if (tid >= 64) return;
+    const int lane = tid;
+    if ((a.flags & CP_FLAG_DELAY_INJECT) && ((id * 2654435761u) >> 30) == 0) {
+        const uint64_t s = wall_clock64();
+        while (wall_clock64() - s < 2000) __builtin_amdgcn_s_sleep(8);  // ~20 us
+    }
+    if (a.trace && lane == 0) a.trace[4 * (size_t)id + 3] = wall_clock64();
+    const int beg = a.dep_off[id], end = a.dep_off[id + 1];
+    for (int e0 = beg; e0 < end; e0 += 64) {
+        const int e = e0 + lane;
+        bool ready = false;
+        uint32_t c = 0;
+        if (e < end) {
+            c = (uint32_t)a.dep_ids[e];
+            const int old = __hip_atomic_fetch_sub(a.score + c, 1, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+            ready = (old == 1);
+        }
+        const uint64_t mask = __ballot(ready);
+        if (mask) {
+            const int leader = __ffsll((unsigned long long)mask) - 1;
+            uint32_t base = 0;
+            if (lane == leader)
+                base = __hip_atomic_fetch_add(a.ctl + kCtlTail, (uint32_t)__popcll(mask),
+                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            base = __shfl(base, leader);
+            if (ready) {
+                const uint32_t rank = (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
+                __hip_atomic_store(a.queue + base + rank, c, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ void decode(const ChainArgs &a, uint32_t id, int &l, int &i, int &j) {
+    l = 0;
+    while (l + 1 < a.L && (int)id >= a.layer[l + 1].tile_off) ++l;
+    const int loc = (int)id - a.layer[l].tile_off;
+    i = loc / a.layer[l].nbn;
+    j = loc - i * a.layer[l].nbn;
+}
+
+// ----------------------------------------------------------------------------
+// Kernels
+// ----------------------------------------------------------------------------
+
+// Persistent worker: loop prologue -> tile body -> publish until the queue is
+// exhausted.  Grid = number of workers (<= co-resident workgroups).
+template <class Body>
+__global__ void __launch_bounds__(kThreads) worker_kernel(ChainArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[Body::LDS];
+    __shared__ uint32_t s_id;
+    for (;;) {
+        if (threadIdx.x == 0) s_id = prologue(a);
+        __syncthreads();
+        const uint32_t id = s_id;
+        if (id >= (uint32_t)a.T) break;
+        int l, i, j;
+        decode(a, id, l, i, j);
+        Body::run(a.layer[l], i, j, lds);
+        if (a.trace && threadIdx.x == 0) a.trace[4 * (size_t)id + 2] = wall_clock64();
+        if (l + 1 < a.L) {
+            publish(a, id);
+        }
+        __syncthreads();  // s_id is rewritten by the next prologue
+    }
+}
+
+// One layer, one tile per workgroup, row-blocks [rb0, rb0 + nrb): the plain
+// kernel-boundary execution used by the sequential and micro-batched modes.
+template <class Body>
+__global__ void __launch_bounds__(kThreads) layer_kernel(ChainArgs a, int l, int rb0) {
+    __shared__ __attribute__((aligned(16))) char lds[Body::LDS];
+    const LayerDesc &d = a.layer[l];
+    const int t = blockIdx.x;
+    const int i = rb0 + t / d.nbn, j = t % d.nbn;
+    Body::run(d, i, j, lds);
+}
+
+// Per-run state reset: scoreboard from the in-degree template, queue
+// pre-filled with the first layer's tiles (row-block-major) and EMPTY after.
+__global__ void reset_kernel(ChainArgs a, int n_first) {
+    const int stride = gridDim.x * blockDim.x;
+    for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < a.T; t += stride) {
+        a.score[t] = a.indeg[t];
+        a.queue[t] = t < n_first ? (uint32_t)t : kEmpty;
+        if (a.deq_count) a.deq_count[t] = 0;
+        if (a.trace) {
+            a.trace[4 * (size_t)t + 0] = 0;
+            a.trace[4 * (size_t)t + 1] = 0;
+            a.trace[4 * (size_t)t + 2] = 0;
+            a.trace[4 * (size_t)t + 3] = 0;
+        }
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        a.ctl[kCtlHead] = 0;
+        a.ctl[kCtlTail] = (uint32_t)n_first;
+        a.ctl[kCtlStatus] = 0;
+    }
+}
+
+// Fill an intermediate with quiet NaN so that a premature read is visible.
+__global__ void poison_kernel(uint32_t *p, size_t words, uint32_t pattern) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t w = (size_t)blockIdx.x * blockDim.x + threadIdx.x; w < words; w += stride)
+        p[w] = pattern;
+}
+
+// ----------------------------------------------------------------------------
+// Launchers and the variant table
+// ----------------------------------------------------------------------------
+template <class Body>
+hipError_t launch_worker_t(const ChainArgs &a, int grid, hipStream_t s) {
+    hipLaunchKernelGGL(worker_kernel<Body>, dim3(grid), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+template <class Body>
+hipError_t launch_layer_t(const ChainArgs &a, int l, int rb0, int nrb, hipStream_t s) {
+    const int grid = nrb * a.layer[l].nbn;
+    if (grid <= 0) return hipSuccess;
+    hipLaunchKernelGGL(layer_kernel<Body>, dim3(grid), dim3(kThreads), 0, s, a, l, rb0);
+    return hipGetLastError();
+}
+
+template <class Body>
+hipError_t occupancy_t(int *blocks) {
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, worker_kernel<Body>, kThreads, 0);
+}
+
+#define CP_BF16_VARIANT(bm, bn)                                                                 \
+    {CP_BF16, bm, bn, 64, Bf16Body<bm, bn>::LDS, launch_worker_t<Bf16Body<bm, bn>>,          \
+     launch_layer_t<Bf16Body<bm, bn>>, occupancy_t<Bf16Body<bm, bn>>}
+
+static const Variant kVariants[] = {
+    {CP_F32, 64, 64, 32, F32Body::LDS, launch_worker_t<F32Body>, launch_layer_t<F32Body>,
+     occupancy_t<F32Body>},
+    CP_BF16_VARIANT(256, 256), CP_BF16_VARIANT(256, 128), CP_BF16_VARIANT(128, 256),
+    CP_BF16_VARIANT(128, 128), CP_BF16_VARIANT(256, 64),  CP_BF16_VARIANT(64, 256),
+    CP_BF16_VARIANT(128, 64),  CP_BF16_VARIANT(64, 128),  CP_BF16_VARIANT(64, 64),
+};
+
+const Variant *find_variant(int dtype, int tile_m, int tile_n) {
+    for (const Variant &v : kVariants)
+        if (v.dtype == dtype && v.tile_m == tile_m && v.tile_n == tile_n) return &v;
+    return nullptr;
+}
+
+const Variant *variant_list(int *count) {
+    *count = (int)(sizeof(kVariants) / sizeof(kVariants[0]));
+    return kVariants;
+}
+
+hipError_t launch_reset(const ChainArgs &a, int n_first, hipStream_t s) {
+    int grid = (a.T + kThreads - 1) / kThreads;
+    if (grid > 1024) grid = 1024;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL(reset_kernel, dim3(grid), dim3(kThreads), 0, s, a, n_first);
+    return hipGetLastError();
+}
+
+hipError_t launch_poison(void *p, size_t bytes, int dtype, hipStream_t s) {
+    const size_t words = bytes / 4;
+    if (words == 0) return hipSuccess;
+    const uint32_t pattern = dtype == CP_BF16 ? 0x7FC07FC0u : 0x7FC00000u;
+    size_t grid = (words + kThreads - 1) / kThreads;
+    if (grid > 2048) grid = 2048;
+    hipLaunchKernelGGL(poison_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s,
+                       static_cast<uint32_t *>(p), words, pattern);
+    return hipGetLastError();
+}
+
+}  // namespace cp

@@ -1,0 +1,23 @@
+"""Launch configuration of each workload: tile shape and micro-batch chunk
+sizes.  Used by the benchmark and by the parity tests, so that the tests
+check exactly the configuration that is timed."""
+
+# (tile_m, tile_n) per workload key of inputs.CONFIGS
+TILES = {
+    "c1": (64, 64),
+    "c2": (128, 128),
+    "c3": (256, 256),
+    "c4": (256, 256),
+    "c5": (64, 256),
+}
+
+# rows per chunk swept by the micro-batched baseline (each a multiple of tile_m
+# that divides M and leaves at least two chunks)
+def chunk_sweep(M: int, tile_m: int):
+    out = []
+    m = tile_m
+    while m < M:
+        if M % m == 0:
+            out.append(m)
+        m *= 2
+    return out
