@@ -188,12 +188,13 @@ def test_edge_shapes(rt, case):
 
 
 def test_many_tiles_many_waves(rt):
-    """More tiles than workers, ragged last wave (T % workers != 0)."""
-    M, widths = 1536, (512, 1088 + 64 * 3, 576)   # 24 row-blocks of 64
-    X, Ws = gen.chain_inputs(M, widths, gen.BF16, 1.0, (1 / np.sqrt(512), 1 / np.sqrt(1280)), 81)
+    """More tiles than persistent workers, so workers loop over several
+    tiles and the last wave is ragged."""
+    M, widths = 4096, (256, 1024, 320)   # 64 row-blocks of 64: 1024 + 320 tiles
+    X, Ws = gen.chain_inputs(M, widths, gen.BF16, 1.0, (1 / 16, 1 / 32), 81)
     out, st = run_modes(rt, X, Ws, gen.BF16, (64, 64), flags=all_flags(), reps=2)
     say("workers", st["n_workers"], "tiles", st["n_tiles"])
-    assert st["n_tiles"] % st["n_workers"] != 0
+    assert st["n_tiles"] > st["n_workers"]
     ref = oracle.chain(X, Ws, gen.BF16)
     assert oracle.rel_err(as_values(out["pipelined"], gen.BF16), ref) <= TOL[gen.BF16]
     assert same_bits(out["pipelined"], out["sequential"])

@@ -251,8 +251,10 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
         return fail(CP_ERR_INVALID_ARG, "CP_FLAG_STARVE_LAST needs at least two layers");
 
     int ndev = 0;
-    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0)
-        return fail(CP_ERR_NO_DEVICE, "no HIP device visible");
+    const hipError_t de = hipGetDeviceCount(&ndev);
+    if (de != hipSuccess || ndev <= 0)
+        return fail(CP_ERR_NO_DEVICE, "no HIP device visible (hipGetDeviceCount: %s, count %d)",
+                    hipGetErrorString(de), ndev);
 
     cp_chain *p = new (std::nothrow) cp_chain();
     if (!p) return fail(CP_ERR_OOM, "host allocation failed");

@@ -63,6 +63,15 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python -m tile_dependency_pipelined_amd.build` "
                       "(the chain has no CPU fallback)")
 
+# PyTorch must load its HIP runtime before this library is opened: opened
+# first, the library's runtime instance and PyTorch's end up separate and the
+# second one to initialise sees no device.  Loading torch first makes both
+# share one runtime, so PyTorch's streams and allocations are valid here.
+try:
+    import torch  # noqa: F401
+except ImportError:  # a C-only user of the library; its own runtime then serves
+    torch = None
+
 _lib = ctypes.CDLL(LIB_PATH)
 _vp, _i32, _i64, _u32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32
 _pi32 = ctypes.POINTER(ctypes.c_int32)
