@@ -53,36 +53,60 @@ __device__ __forceinline__ float act_apply(float x, int act) {
 // ----------------------------------------------------------------------------
 // bf16 tile body: C[BM x BN] tile (i, j) of A[M][K] . W[K][N], BK = 64.
 //
-// LDS holds both operands "k-contiguous": A as [BM][64] and W transposed to
-// [BN][64], 128 bytes per row, in 16-byte chunks XOR-swizzled by
-// sw(r) = (r ^ (r >> 3)) & 7 so that the fragment reads (8 consecutive rows,
-// same chunk), the A stores (one row, 8 chunks) and the transposed W stores
-// (rows 8 apart) all touch 32 distinct banks.
-// W is row-major [K][N] (n contiguous): each thread loads BN/32 rows of one
-// 16-byte column chunk and transposes that (BN/32) x 8 block in registers.
+// Both operands travel HBM -> LDS by 16-byte direct loads (global_load_lds):
+// lane l of a load lands at LDS base + 16 l, so no VGPR staging and no LDS
+// store instructions are needed; the swizzle below is applied by choosing
+// which global 16-byte chunk each lane fetches.
+//   A tile [BM][64] bf16, 128-byte rows, chunk c of row r stored at chunk
+//     position c ^ (r & 7): the MFMA A fragment (8 consecutive k of one row)
+//     is one ds_read_b128, 8 consecutive rows hit 8 distinct bank groups.
+//   W tile [64][BN] bf16 in its natural n-contiguous layout, chunk c of row k
+//     stored at c ^ 2 (k & 3).  The B fragment (8 consecutive k of one column)
+//     is read by two ds_read_b64_tr_b16: within a group of 16 lanes, result
+//     lane i, element j is element (i mod 4) of the 8 bytes addressed by lane
+//     4 j + i / 4, so lane s addresses row k0 + s/4, columns n0 + 4 (s mod 4)
+//     and lane i receives W[k0 .. k0+3][n0 + i].
+// Two LDS stages: the loads of slab s+1 are in flight while slab s is
+// multiplied.
 // ----------------------------------------------------------------------------
-__device__ __forceinline__ int sw(int r) { return (r ^ (r >> 3)) & 7; }
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// wait until at most N vector-memory operations of this wave are in flight
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
 template <int BM_, int BN_>
 struct Bf16Body {
     static constexpr int BM = BM_, BN = BN_, BK = 64;
     static constexpr int WM = BM / 2, WN = BN / 2;   // per-wave sub-tile (2 x 2 waves)
     static constexpr int FM = WM / 32, FN = WN / 32; // 32x32 MFMA blocks per wave
-    static constexpr int A_LD = BM * 8 / kThreads;  // 16-byte A loads per thread
-    static constexpr int NCH = BN / 8;               // 16-byte chunks per W row
-    static constexpr int KR = BK * NCH / kThreads;   // W rows per thread (= BN/32)
-    static constexpr int STAGE = (BM + BN) * BK * 2; // bytes per LDS stage
-    static constexpr int LDS = 2 * STAGE;
+    static constexpr int RB = BN * 2;                // bytes per W row in LDS
+    static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * RB;
+    static constexpr int A_PW = A_BYTES / 1024 / 4;  // 1 KiB direct loads per wave (A)
+    static constexpr int B_PW = B_BYTES / 1024 / 4;  // (W)
+    static constexpr int STAGE = A_BYTES + B_BYTES;  // bytes of one LDS stage
     static_assert(BM >= 64 && BN >= 64 && BM <= 256 && BN <= 256, "tile");
-    static_assert(KR >= 2 && KR <= 8 && (KR & 1) == 0, "W rows per thread");
+    static_assert(A_PW >= 1 && B_PW >= 1, "loads per wave");
 
-    __device__ static void run(const LayerDesc &d, int i, int j, char *lds) {
+    __device__ static int fb(int k) { return (k & 3) << 1; }
+
+    // stage0 / stage1 must be two distinct __shared__ arrays: the compiler
+    // then knows that loads in flight into one stage do not alias reads of
+    // the other and does not wait for them before reading.
+    __device__ __forceinline__ static void run(const LayerDesc &d, int i, int j, char *stage0,
+                                               char *stage1) {
         const uint16_t *__restrict__ A = static_cast<const uint16_t *>(d.A);
         const uint16_t *__restrict__ W = static_cast<const uint16_t *>(d.W);
         uint16_t *__restrict__ C = static_cast<uint16_t *>(d.C);
         const int K = d.K, N = d.N;
         const int row0 = i * BM, col0 = j * BN;
-        const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+        const int tid = threadIdx.x, lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int wm = wave >> 1, wn = wave & 1;
 
         f32x16_t acc[FM][FN];
@@ -93,66 +117,60 @@ struct Bf16Body {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.0f;
 
-        // global addressing
-        const uint16_t *a_src = A + (size_t)(row0 + (tid >> 3)) * K + (tid & 7) * 8;
-        const int b_nch = tid % NCH, b_kg = tid / NCH;
-        const uint16_t *b_src = W + (size_t)(b_kg * KR) * N + col0 + b_nch * 8;
+        // per-lane source offsets (elements) of this wave's direct loads
+        uint32_t a_off[A_PW], b_off[B_PW];
+#pragma unroll
+        for (int q = 0; q < A_PW; ++q) {
+            const int o = (q * 4 + wave) * 1024 + lane * 16;  // byte in the A region
+            const int r = o >> 7, c = ((o >> 4) & 7) ^ (r & 7);
+            a_off[q] = (uint32_t)((row0 + r) * K + c * 8);
+        }
+#pragma unroll
+        for (int q = 0; q < B_PW; ++q) {
+            const int o = (q * 4 + wave) * 1024 + lane * 16;  // byte in the W region
+            const int k = o / RB, c = ((o % RB) >> 4) ^ fb(o / RB);
+            b_off[q] = (uint32_t)(k * N + col0 + c * 8);
+        }
 
-        uint4 ra[A_LD], rb[KR];
-        auto gload = [&](int k0) {
+        auto issue = [&](char *As, int k0) {
+            char *Bs = As + A_BYTES;
 #pragma unroll
-            for (int q = 0; q < A_LD; ++q)
-                ra[q] = *reinterpret_cast<const uint4 *>(a_src + (size_t)q * 32 * K + k0);
+            for (int q = 0; q < A_PW; ++q)
+                __builtin_amdgcn_global_load_lds(A + a_off[q] + k0,
+                                                 (lds_void_t *)(As + (q * 4 + wave) * 1024), 16, 0, 0);
+            const uint16_t *Wk = W + (size_t)k0 * N;
 #pragma unroll
-            for (int kk = 0; kk < KR; ++kk)
-                rb[kk] = *reinterpret_cast<const uint4 *>(b_src + (size_t)(k0 + kk) * N);
+            for (int q = 0; q < B_PW; ++q)
+                __builtin_amdgcn_global_load_lds(Wk + b_off[q],
+                                                 (lds_void_t *)(Bs + (q * 4 + wave) * 1024), 16, 0, 0);
         };
-        auto lstore = [&](int buf) {
-            char *As = lds + buf * STAGE;
-            char *Bs = As + BM * BK * 2;
-#pragma unroll
-            for (int q = 0; q < A_LD; ++q) {
-                const int r = q * 32 + (tid >> 3);
-                *reinterpret_cast<uint4 *>(As + r * 128 + (((tid & 7) ^ sw(r)) << 4)) = ra[q];
-            }
-            const int kb = b_kg * KR;  // first k of this thread's rows within the slab
-            const int lch = kb >> 3, within = (kb & 7) * 2;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int n = b_nch * 8 + e;
-                char *dst = Bs + n * 128 + ((lch ^ sw(n)) << 4) + within;
-                uint32_t w[KR / 2];
-#pragma unroll
-                for (int p = 0; p < KR / 2; ++p) {
-                    const uint32_t lo = reinterpret_cast<const uint32_t *>(&rb[2 * p])[e >> 1];
-                    const uint32_t hi = reinterpret_cast<const uint32_t *>(&rb[2 * p + 1])[e >> 1];
-                    w[p] = (e & 1) ? ((lo >> 16) | (hi & 0xFFFF0000u)) : ((lo & 0xFFFFu) | (hi << 16));
-                }
-                if constexpr (KR == 8) {
-                    *reinterpret_cast<uint4 *>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
-                } else if constexpr (KR == 4) {
-                    *reinterpret_cast<uint2 *>(dst) = make_uint2(w[0], w[1]);
-                } else {
-                    *reinterpret_cast<uint32_t *>(dst) = w[0];
-                }
-            }
-        };
-        auto compute = [&](int buf) {
-            const char *As = lds + buf * STAGE;
-            const char *Bs = As + BM * BK * 2;
+
+        // fragment addresses that do not depend on the stage or k step
+        const int g = lane >> 5;                       // k half of the fragment
+        const int s4 = (lane & 15) >> 2;               // row within a transpose group
+        const int nb = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        auto compute = [&](const char *As) {
+            const char *Bs = As + A_BYTES;
 #pragma unroll
             for (int kk = 0; kk < BK / 16; ++kk) {
-                const int c = kk * 2 + (lane >> 5);
+                const int c = kk * 2 + g;
                 bf16x8_t af[FM], bfv[FN];
 #pragma unroll
                 for (int fm = 0; fm < FM; ++fm) {
                     const int r = wm * WM + fm * 32 + (lane & 31);
-                    af[fm] = *reinterpret_cast<const bf16x8_t *>(As + r * 128 + ((c ^ sw(r)) << 4));
+                    af[fm] = *reinterpret_cast<const bf16x8_t *>(As + r * 128 + ((c ^ (r & 7)) << 4));
                 }
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn) {
-                    const int n = wn * WN + fn * 32 + (lane & 31);
-                    bfv[fn] = *reinterpret_cast<const bf16x8_t *>(Bs + n * 128 + ((c ^ sw(n)) << 4));
+                    const int n = wn * WN + fn * 32 + nb;
+                    const int k = kk * 16 + 8 * g + s4;
+                    const int cn = n >> 3, half = ((n >> 2) & 1) * 8;
+                    const char *p0 = Bs + k * RB + ((cn ^ fb(k)) << 4) + half;
+                    const char *p1 = Bs + (k + 4) * RB + ((cn ^ fb(k + 4)) << 4) + half;
+                    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)p0);
+                    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)p1);
+                    const v4i16_t both[2] = {lo, hi};
+                    bfv[fn] = *reinterpret_cast<const bf16x8_t *>(both);
                 }
                 // W fragment as the first operand: the result holds, per lane,
                 // output row m = lane%32 and four consecutive output columns.
@@ -166,15 +184,30 @@ struct Bf16Body {
         };
 
         const int nk = K / BK;
-        gload(0);
-        lstore(0);
+        issue(stage0, 0);
+        wait_vmcnt<0>();
         __syncthreads();
-        for (int ks = 0; ks < nk; ++ks) {
-            if (ks + 1 < nk) gload((ks + 1) * BK);
-            compute(ks & 1);
-            if (ks + 1 < nk) lstore((ks + 1) & 1);
+        int ks = 0;
+        for (; ks + 2 < nk; ks += 2) {  // slabs ks (stage0) and ks+1 (stage1), prefetching ks+1, ks+2
+            issue(stage1, (ks + 1) * BK);
+            compute(stage0);
+            wait_vmcnt<0>();
+            __syncthreads();
+            issue(stage0, (ks + 2) * BK);
+            compute(stage1);
+            wait_vmcnt<0>();
             __syncthreads();
         }
+        if (ks + 1 < nk) {  // two slabs left
+            issue(stage1, (ks + 1) * BK);
+            compute(stage0);
+            wait_vmcnt<0>();
+            __syncthreads();
+            compute(stage1);
+        } else {            // one slab left
+            compute(stage0);
+        }
+        __syncthreads();
 
         // epilogue: activation on the fp32 accumulator, RNE to bf16, 8-byte stores
         const int act = d.act;
@@ -185,13 +218,13 @@ struct Bf16Body {
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int n = fn * 32 + g * 8 + (lane >> 5) * 4;
+                for (int gq = 0; gq < 4; ++gq) {
+                    const int n = fn * 32 + gq * 8 + (lane >> 5) * 4;
                     const f32x16_t &v = acc[fm][fn];
-                    const uint32_t b0 = f32_to_bf16_rne(act_apply(v[4 * g + 0], act));
-                    const uint32_t b1 = f32_to_bf16_rne(act_apply(v[4 * g + 1], act));
-                    const uint32_t b2 = f32_to_bf16_rne(act_apply(v[4 * g + 2], act));
-                    const uint32_t b3 = f32_to_bf16_rne(act_apply(v[4 * g + 3], act));
+                    const uint32_t b0 = f32_to_bf16_rne(act_apply(v[4 * gq + 0], act));
+                    const uint32_t b1 = f32_to_bf16_rne(act_apply(v[4 * gq + 1], act));
+                    const uint32_t b2 = f32_to_bf16_rne(act_apply(v[4 * gq + 2], act));
+                    const uint32_t b3 = f32_to_bf16_rne(act_apply(v[4 * gq + 3], act));
                     *reinterpret_cast<uint2 *>(crow + n) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
                 }
         }
@@ -208,9 +241,9 @@ struct F32Body {
     static constexpr int AP = BM + 1;  // padded A row ([k][m])
     static constexpr int BP = BN + 4;  // padded W row ([k][n]), keeps 16-byte alignment
     static constexpr int STAGE = (BK * AP + BK * BP) * 4;
-    static constexpr int LDS = 2 * STAGE;
 
-    __device__ static void run(const LayerDesc &d, int i, int j, char *lds) {
+    __device__ __forceinline__ static void run(const LayerDesc &d, int i, int j, char *stage0,
+                                               char *stage1) {
         const float *__restrict__ A = static_cast<const float *>(d.A);
         const float *__restrict__ W = static_cast<const float *>(d.W);
         float *__restrict__ C = static_cast<float *>(d.C);
@@ -234,7 +267,7 @@ struct F32Body {
             }
         };
         auto lstore = [&](int buf) {
-            float *As = reinterpret_cast<float *>(lds + buf * STAGE);
+            float *As = reinterpret_cast<float *>(buf ? stage1 : stage0);
             float *Bs = As + BK * AP;
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
@@ -248,7 +281,7 @@ struct F32Body {
             }
         };
         auto compute = [&](int buf) {
-            const float *As = reinterpret_cast<const float *>(lds + buf * STAGE);
+            const float *As = reinterpret_cast<const float *>(buf ? stage1 : stage0);
             const float *Bs = As + BK * AP;
 #pragma unroll
             for (int kk = 0; kk < BK / 2; ++kk) {
@@ -389,7 +422,8 @@ __device__ __forceinline__ void decode(const ChainArgs &a, uint32_t id, int &l, 
 // exhausted.  Grid = number of workers (<= co-resident workgroups).
 template <class Body>
 __global__ void __launch_bounds__(kThreads) worker_kernel(ChainArgs a) {
-    __shared__ __attribute__((aligned(16))) char lds[Body::LDS];
+    __shared__ __attribute__((aligned(1024))) char stage0[Body::STAGE];
+    __shared__ __attribute__((aligned(1024))) char stage1[Body::STAGE];
     __shared__ uint32_t s_id;
     for (;;) {
         if (threadIdx.x == 0) s_id = prologue(a);
@@ -398,7 +432,7 @@ __global__ void __launch_bounds__(kThreads) worker_kernel(ChainArgs a) {
         if (id >= (uint32_t)a.T) break;
         int l, i, j;
         decode(a, id, l, i, j);
-        Body::run(a.layer[l], i, j, lds);
+        Body::run(a.layer[l], i, j, stage0, stage1);
         if (a.trace && threadIdx.x == 0) a.trace[4 * (size_t)id + 2] = wall_clock64();
         if (l + 1 < a.L) {
             publish(a, id);
@@ -411,11 +445,12 @@ __global__ void __launch_bounds__(kThreads) worker_kernel(ChainArgs a) {
 // kernel-boundary execution used by the sequential and micro-batched modes.
 template <class Body>
 __global__ void __launch_bounds__(kThreads) layer_kernel(ChainArgs a, int l, int rb0) {
-    __shared__ __attribute__((aligned(16))) char lds[Body::LDS];
+    __shared__ __attribute__((aligned(1024))) char stage0[Body::STAGE];
+    __shared__ __attribute__((aligned(1024))) char stage1[Body::STAGE];
     const LayerDesc &d = a.layer[l];
     const int t = blockIdx.x;
     const int i = rb0 + t / d.nbn, j = t % d.nbn;
-    Body::run(d, i, j, lds);
+    Body::run(d, i, j, stage0, stage1);
 }
 
 // Per-run state reset: scoreboard from the in-degree template, queue
@@ -470,11 +505,11 @@ hipError_t occupancy_t(int *blocks) {
 }
 
 #define CP_BF16_VARIANT(bm, bn)                                                                 \
-    {CP_BF16, bm, bn, 64, Bf16Body<bm, bn>::LDS, launch_worker_t<Bf16Body<bm, bn>>,          \
+    {CP_BF16, bm, bn, 64, 2 * Bf16Body<bm, bn>::STAGE, launch_worker_t<Bf16Body<bm, bn>>,          \
      launch_layer_t<Bf16Body<bm, bn>>, occupancy_t<Bf16Body<bm, bn>>}
 
 static const Variant kVariants[] = {
-    {CP_F32, 64, 64, 32, F32Body::LDS, launch_worker_t<F32Body>, launch_layer_t<F32Body>,
+    {CP_F32, 64, 64, 32, 2 * F32Body::STAGE, launch_worker_t<F32Body>, launch_layer_t<F32Body>,
      occupancy_t<F32Body>},
     CP_BF16_VARIANT(256, 256), CP_BF16_VARIANT(256, 128), CP_BF16_VARIANT(128, 256),
     CP_BF16_VARIANT(128, 128), CP_BF16_VARIANT(256, 64),  CP_BF16_VARIANT(64, 256),
