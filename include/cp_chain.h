@@ -91,7 +91,9 @@ typedef struct cp_chain_stats_t {
     int32_t nonzero_scores;  /* consumers whose counter did not end at 0                  */
     int32_t bad_dequeues;    /* tiles not dequeued exactly once (-1 if not recorded)      */
     int32_t queue_is_perm;   /* 1 if queue[0..T) is a permutation of [0,T)                */
-    uint32_t head, tail;     /* final ticket counter (>= T) and push counter (== T)        */
+    uint32_t head, tail;     /* summed over the queues: tickets taken (>= T), slots filled (== T) */
+    int32_t n_queues;        /* work-queues (one per XCD)                                 */
+    int32_t queues_drained;  /* 1 if every queue was filled to its size and fully taken   */
     int32_t order_violations;/* TRACE only: consumers that started before a producer ended */
     double last_run_ms;      /* elapsed time of the last run, from events on its stream   */
     double last_kernel_ms;   /* pipelined: the persistent launch alone (reset excluded);

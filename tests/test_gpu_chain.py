@@ -67,6 +67,7 @@ def check_invariants(st, flags):
     assert st["queue_is_perm"] == 1, st
     assert st["tail"] == T, st
     assert st["head"] >= T, st
+    assert st["queues_drained"] == 1, st
     if flags & rt_flags()["DEBUG"]:
         assert st["bad_dequeues"] == 0, st
     if flags & rt_flags()["TRACE"]:
@@ -220,7 +221,7 @@ def test_watchdog_timeout_is_reported(rt):
         st = c.stats(check=False)
         say("watchdog stats", st)
         assert st["rc"] == nat.CP_ERR_TIMEOUT and st["status"] == nat.CP_ERR_TIMEOUT
-        assert st["tail"] == st["n_tiles"] - 1
+        assert st["tail"] == st["n_tiles"] - 1 and st["queues_drained"] == 0
         # the plan is reusable afterwards in the other modes
         c.run(dX, dW, dY, mode="sequential")
         assert c.stats()["status"] == 0

@@ -119,10 +119,13 @@ struct cp_chain {
     const cp::Variant *var = nullptr;
     TileGraph g;
     int n_workers = 0;
+    int nq = 1;                        // work-queues (one per XCD, at most kMaxQueues)
+    int32_t qbase[cp::kMaxQueues] = {}, qsize[cp::kMaxQueues] = {}, qfirst[cp::kMaxQueues] = {};
+    bool coop = true;                  // cooperative launch of the persistent grid
     // device state (one allocation) and intermediates
     char *state = nullptr;
     int32_t *d_score = nullptr, *d_indeg = nullptr, *d_dep_off = nullptr, *d_dep_ids = nullptr;
-    uint32_t *d_queue = nullptr, *d_ctl = nullptr, *d_deq = nullptr;
+    uint32_t *d_queue = nullptr, *d_ctl = nullptr, *d_deq = nullptr, *d_qinit = nullptr;
     uint64_t *d_trace = nullptr;
     void *inter[CP_MAX_LAYERS] = {};
     size_t inter_bytes[CP_MAX_LAYERS] = {};
@@ -174,6 +177,13 @@ cp::ChainArgs make_args(const cp_chain *p, const void *X, const void *const *W, 
     a.L = p->L;
     a.T = p->g.T;
     a.flags = p->flags;
+    a.nq = p->nq;
+    for (int q = 0; q < cp::kMaxQueues; ++q) {
+        a.qbase[q] = p->qbase[q];
+        a.qsize[q] = p->qsize[q];
+        a.qfirst[q] = p->qfirst[q];
+    }
+    a.qinit = p->d_qinit;
     a.queue = p->d_queue;
     a.ctl = p->d_ctl;
     a.score = p->d_score;
@@ -290,6 +300,7 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
     const size_t o_doff = off;    off = align_up(off + (T + 1) * 4, 256);
     const size_t o_dids = off;    off = align_up(off + E * 4, 256);
     const size_t o_deq = off;     off = align_up(off + T * 4, 256);
+    const size_t o_qinit = off;   off = align_up(off + T * 4, 256);
     const size_t o_trace = off;   off = align_up(off + ((flags & CP_FLAG_TRACE) ? T * 32 : 0), 256);
     int rc2 = [&]() -> int {
         CP_HIP(hipMalloc(&p->state, off));
@@ -300,6 +311,7 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
         p->d_dep_off = reinterpret_cast<int32_t *>(p->state + o_doff);
         p->d_dep_ids = reinterpret_cast<int32_t *>(p->state + o_dids);
         p->d_deq = reinterpret_cast<uint32_t *>(p->state + o_deq);
+        p->d_qinit = reinterpret_cast<uint32_t *>(p->state + o_qinit);
         p->d_trace = (flags & CP_FLAG_TRACE) ? reinterpret_cast<uint64_t *>(p->state + o_trace) : nullptr;
         CP_HIP(hipMemset(p->state, 0, off));
         CP_HIP(hipMemcpy(p->d_indeg, g.indeg.data(), T * 4, hipMemcpyHostToDevice));
@@ -321,6 +333,31 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
         CP_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device));
         if (per_cu < 1) return fail(CP_ERR_UNSUPPORTED, "kernel cannot be resident (occupancy 0)");
         p->n_workers = std::max(1, std::min(per_cu * cus, g.T));
+        int coop_ok = 0;
+        if (hipDeviceGetAttribute(&coop_ok, hipDeviceAttributeCooperativeLaunch, p->device) != hipSuccess)
+            coop_ok = 0;
+        p->coop = coop_ok != 0;
+        // one queue per XCD; a tile belongs to the queue of its column panel
+        int xcds = 8;
+        p->nq = std::max(1, std::min({cp::kMaxQueues, xcds, p->n_workers}));
+        std::vector<std::vector<uint32_t>> first(p->nq);
+        std::vector<int32_t> size(p->nq, 0);
+        for (int l = 0; l < n_layers; ++l)
+            for (int32_t t = g.layer_off[l]; t < g.layer_off[l + 1]; ++t) {
+                const int q = ((t - g.layer_off[l]) % g.nbn[l]) % p->nq;
+                ++size[q];
+                if (l == 0) first[q].push_back((uint32_t)t);  // row-block-major
+            }
+        std::vector<uint32_t> qinit((size_t)g.T, cp::kEmpty);
+        int32_t base = 0;
+        for (int q = 0; q < p->nq; ++q) {
+            p->qbase[q] = base;
+            p->qsize[q] = size[q];
+            p->qfirst[q] = (int32_t)first[q].size();
+            std::copy(first[q].begin(), first[q].end(), qinit.begin() + base);
+            base += size[q];
+        }
+        CP_HIP(hipMemcpy(p->d_qinit, qinit.data(), T * 4, hipMemcpyHostToDevice));
         int clk_khz = 0;
         if (hipDeviceGetAttribute(&clk_khz, hipDeviceAttributeWallClockRate, p->device) == hipSuccess &&
             clk_khz > 0)
@@ -357,9 +394,9 @@ int cp_chain_run(cp_chain *p, const void *X, const void *const *W, void *Y, void
     if (p->flags & CP_FLAG_POISON)
         for (int l = 0; l + 1 < p->L; ++l) CP_HIP(cp::launch_poison(p->inter[l], p->inter_bytes[l], p->dtype, s));
     if (mode == CP_MODE_PIPELINED) {
-        CP_HIP(cp::launch_reset(a, p->g.P1, s));
+        CP_HIP(cp::launch_reset(a, s));
         CP_HIP(hipEventRecord(p->ev_kernel, s));
-        CP_HIP(p->var->launch_worker(a, p->n_workers, s));
+        CP_HIP(p->var->launch_worker(a, p->n_workers, p->coop, s));
     } else if (mode == CP_MODE_SEQUENTIAL) {
         const int nrb = (int)(p->M / p->tile_m);
         for (int l = 0; l < p->L; ++l) CP_HIP(p->var->launch_layer(a, l, 0, nrb, s));
@@ -392,6 +429,7 @@ int cp_chain_stats(cp_chain *p, cp_chain_stats_t *out) {
     out->n_first = p->g.P1;
     out->n_edges = p->g.E;
     out->n_workers = p->n_workers;
+    out->n_queues = p->nq;
     out->tile_m = p->tile_m;
     out->tile_n = p->tile_n;
     out->bad_dequeues = -1;
@@ -414,8 +452,14 @@ int cp_chain_stats(cp_chain *p, cp_chain_stats_t *out) {
     CP_HIP(hipMemcpy(score.data(), p->d_score, T * 4, hipMemcpyDeviceToHost));
     CP_HIP(hipMemcpy(queue.data(), p->d_queue, T * 4, hipMemcpyDeviceToHost));
     out->status = (int32_t)ctl[cp::kCtlStatus];
-    out->head = ctl[cp::kCtlHead];
-    out->tail = ctl[cp::kCtlTail];
+    out->n_queues = p->nq;
+    out->queues_drained = 1;
+    for (int q = 0; q < p->nq; ++q) {
+        const uint32_t h = ctl[cp::ctl_head(q)], t = ctl[cp::ctl_tail(q)];
+        out->head += h;
+        out->tail += t;
+        if (t != (uint32_t)p->qsize[q] || h < (uint32_t)p->qsize[q]) out->queues_drained = 0;
+    }
     int32_t nz = 0;
     for (size_t t = 0; t < T; ++t) nz += score[t] != 0;
     out->nonzero_scores = nz;

@@ -11,12 +11,19 @@ constexpr int kThreads = 256;              // 4 wave64 per workgroup
 constexpr uint32_t kEmpty = 0xFFFFFFFFu;   // queue slot not yet filled
 constexpr uint32_t kDone = 0xFFFFFFFEu;    // prologue: no more work
 
-// Control words, each on its own 128-byte line so that the ticket counter,
-// the push counter and the status flag do not share a cache line.
-constexpr int kCtlHead = 0;     // next ticket (slot) to hand out
-constexpr int kCtlTail = 32;    // next free queue slot for a push
-constexpr int kCtlStatus = 64;  // 0 = ok, else a CP_ERR_* code
-constexpr int kCtlWords = 96;
+// Work-queues.  The paper keeps one workqueue per consumer device; here the
+// unit with a private cache is the XCD (8 per MI355X, each with its own L2),
+// so there is one queue per XCD.  A tile belongs to the queue of its column
+// panel (j mod nq): the weight panel it reads then stays in one XCD's L2.
+constexpr int kMaxQueues = 8;
+
+// Control words, each on its own 128-byte line: per queue a ticket counter
+// (head) and a push counter (tail), then the run status.
+constexpr int kCtlLine = 32;                               // words per line
+__host__ __device__ constexpr int ctl_head(int q) { return (2 * q) * kCtlLine; }
+__host__ __device__ constexpr int ctl_tail(int q) { return (2 * q + 1) * kCtlLine; }
+constexpr int kCtlStatus = 2 * kMaxQueues * kCtlLine;      // 0 = ok, else a CP_ERR_* code
+constexpr int kCtlWords = kCtlStatus + kCtlLine;
 
 constexpr int32_t kStatusTimeout = -6;  // == CP_ERR_TIMEOUT
 
@@ -38,23 +45,32 @@ struct ChainArgs {
     int32_t L;           // layers
     int32_t T;           // tiles over all layers
     uint32_t flags;      // CP_FLAG_*
-    int32_t pad0;
-    uint32_t *queue;     // [T] tile IDs in dequeue order (kEmpty until pushed)
-    uint32_t *ctl;       // [kCtlWords] head / tail / status
+    int32_t nq;          // queues in use (1..kMaxQueues)
+    int32_t qbase[kMaxQueues];   // first slot of each queue in `queue`
+    int32_t qsize[kMaxQueues];   // tiles owned by each queue
+    int32_t qfirst[kMaxQueues];  // of which first-layer tiles (pre-filled)
+    uint32_t *queue;     // [T] slots of all queues (kEmpty until pushed)
+    uint32_t *ctl;       // [kCtlWords] per-queue head / tail, status
     int32_t *score;      // [T] remaining producers per tile
     const int32_t *dep_off;  // [T+1] CSR producer -> consumers
     const int32_t *dep_ids;  // [E]
     const int32_t *indeg;    // [T] initial scoreboard (reset source)
+    const uint32_t *qinit;   // [T] initial queue contents (reset source)
     uint32_t *deq_count;     // [T] debug: dequeues per tile, or null
     uint64_t *trace;         // [4T] timestamps, or null
     uint64_t timeout_ticks;  // watchdog on a queue wait, 100 MHz ticks
 };
 
+// Queue that owns tile `id` of layer `l`: its column panel modulo nq.
+__host__ __device__ inline int owner_queue(const LayerDesc &d, int id, int nq) {
+    return ((id - d.tile_off) % d.nbn) % nq;
+}
+
 // A compiled kernel variant (element type x tile shape).
 struct Variant {
     int dtype, tile_m, tile_n, k_step;
     int lds_bytes;
-    hipError_t (*launch_worker)(const ChainArgs &, int grid, hipStream_t);
+    hipError_t (*launch_worker)(const ChainArgs &, int grid, bool cooperative, hipStream_t);
     hipError_t (*launch_layer)(const ChainArgs &, int layer, int rb0, int nrb, hipStream_t);
     hipError_t (*occupancy)(int *blocks_per_cu);
 };
@@ -62,7 +78,7 @@ struct Variant {
 const Variant *find_variant(int dtype, int tile_m, int tile_n);
 const Variant *variant_list(int *count);
 
-hipError_t launch_reset(const ChainArgs &a, int n_first, hipStream_t s);
+hipError_t launch_reset(const ChainArgs &a, hipStream_t s);
 hipError_t launch_poison(void *p, size_t bytes, int dtype, hipStream_t s);
 
 }  // namespace cp

@@ -12,13 +12,14 @@
 // baselines, so all modes produce bit-identical results.
 //
 // gfx950 mapping (MI355X): 256 threads = 4 wave64 per workgroup; bf16 tiles
-// use v_mfma_f32_32x32x16_bf16 with fp32 accumulators, fp32 tiles use
-// v_mfma_f32_32x32x2_f32; operands are staged HBM -> VGPR -> LDS with 128-bit
-// loads and double-buffered LDS; the paper's system-wide threadfence becomes
-// an agent-scope release (L2 write-back, the L2 being private to each XCD)
+// use v_mfma_f32_32x32x16_bf16 with fp32 accumulators held in AGPRs, fp32
+// tiles use v_mfma_f32_32x32x2_f32.  The paper's system-wide threadfence
+// becomes one agent-scope release per tile (write-back of the XCD-private L2)
 // and the consumer's read of the scoreboard an agent-scope acquire.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "cp_chain.h"
 #include "cp_device.h"
@@ -27,6 +28,9 @@ namespace cp {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
 // ----------------------------------------------------------------------------
 // Element conversion and activation (applied to the fp32 accumulator).
@@ -50,8 +54,19 @@ __device__ __forceinline__ float act_apply(float x, int act) {
     return x;
 }
 
+// wait until at most N vector-memory operations of this wave are in flight
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int U>
+using ic = std::integral_constant<int, U>;
+
 // ----------------------------------------------------------------------------
-// bf16 tile body: C[BM x BN] tile (i, j) of A[M][K] . W[K][N], BK = 64.
+// bf16 tile body: C[BM x BN] tile (i, j) of A[M][K] . W[K][N], BK = 64,
+// S-stage LDS pipeline.
 //
 // Both operands travel HBM -> LDS by 16-byte direct loads (global_load_lds):
 // lane l of a load lands at LDS base + 16 l, so no VGPR staging and no LDS
@@ -66,40 +81,31 @@ __device__ __forceinline__ float act_apply(float x, int act) {
 //     lane i, element j is element (i mod 4) of the 8 bytes addressed by lane
 //     4 j + i / 4, so lane s addresses row k0 + s/4, columns n0 + 4 (s mod 4)
 //     and lane i receives W[k0 .. k0+3][n0 + i].
-// Two LDS stages: the loads of slab s+1 are in flight while slab s is
-// multiplied.
+// Pipeline: S-1 slabs are in flight while one is multiplied.  Every stage is
+// its own __shared__ array and every stage index a compile-time constant, so
+// the compiler can tell that loads in flight into one stage do not alias
+// reads of another and does not wait for them before reading.  Past the last
+// slab the prefetch re-reads the last slab into a stage that is never used,
+// which keeps the number of loads in flight, and so the wait, constant.
 // ----------------------------------------------------------------------------
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
-
-// wait until at most N vector-memory operations of this wave are in flight
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-template <int BM_, int BN_>
+template <int BM_, int BN_, int S_>
 struct Bf16Body {
-    static constexpr int BM = BM_, BN = BN_, BK = 64;
+    static constexpr int BM = BM_, BN = BN_, BK = 64, S = S_;
     static constexpr int WM = BM / 2, WN = BN / 2;   // per-wave sub-tile (2 x 2 waves)
     static constexpr int FM = WM / 32, FN = WN / 32; // 32x32 MFMA blocks per wave
     static constexpr int RB = BN * 2;                // bytes per W row in LDS
     static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * RB;
     static constexpr int A_PW = A_BYTES / 1024 / 4;  // 1 KiB direct loads per wave (A)
     static constexpr int B_PW = B_BYTES / 1024 / 4;  // (W)
+    static constexpr int PER = A_PW + B_PW;          // loads per wave per slab
     static constexpr int STAGE = A_BYTES + B_BYTES;  // bytes of one LDS stage
     static_assert(BM >= 64 && BN >= 64 && BM <= 256 && BN <= 256, "tile");
     static_assert(A_PW >= 1 && B_PW >= 1, "loads per wave");
+    static_assert(S >= 2 && S <= 4 && (S - 2) * PER < 64, "stages");
 
     __device__ static int fb(int k) { return (k & 3) << 1; }
 
-    // stage0 / stage1 must be two distinct __shared__ arrays: the compiler
-    // then knows that loads in flight into one stage do not alias reads of
-    // the other and does not wait for them before reading.
-    __device__ __forceinline__ static void run(const LayerDesc &d, int i, int j, char *stage0,
-                                               char *stage1) {
+    __device__ __forceinline__ static void run(const LayerDesc &d, int i, int j, char *const *stg) {
         const uint16_t *__restrict__ A = static_cast<const uint16_t *>(d.A);
         const uint16_t *__restrict__ W = static_cast<const uint16_t *>(d.W);
         uint16_t *__restrict__ C = static_cast<uint16_t *>(d.C);
@@ -146,8 +152,8 @@ struct Bf16Body {
         };
 
         // fragment addresses that do not depend on the stage or k step
-        const int g = lane >> 5;                       // k half of the fragment
-        const int s4 = (lane & 15) >> 2;               // row within a transpose group
+        const int g = lane >> 5;                  // k half of the fragment
+        const int s4 = (lane & 15) >> 2;          // row within a transpose group
         const int nb = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
         auto compute = [&](const char *As) {
             const char *Bs = As + A_BYTES;
@@ -184,29 +190,31 @@ struct Bf16Body {
         };
 
         const int nk = K / BK;
-        issue(stage0, 0);
-        wait_vmcnt<0>();
+        // one pipeline step: prefetch slab+S-1 into the stage freed last step,
+        // multiply slab, wait until slab+1 has landed, publish it to all waves
+        auto step = [&](auto U, int slab) {
+            constexpr int u = decltype(U)::value;
+            const int pre = slab + S - 1 < nk ? slab + S - 1 : nk - 1;
+            issue(stg[(u + S - 1) % S], pre * BK);
+            compute(stg[u]);
+            wait_vmcnt<(S - 2) * PER>();
+            __syncthreads();
+        };
+#pragma unroll
+        for (int u = 0; u < S - 1; ++u) issue(stg[u], (u < nk ? u : nk - 1) * BK);
+        wait_vmcnt<(S - 2) * PER>();
         __syncthreads();
-        int ks = 0;
-        for (; ks + 2 < nk; ks += 2) {  // slabs ks (stage0) and ks+1 (stage1), prefetching ks+1, ks+2
-            issue(stage1, (ks + 1) * BK);
-            compute(stage0);
-            wait_vmcnt<0>();
-            __syncthreads();
-            issue(stage0, (ks + 2) * BK);
-            compute(stage1);
-            wait_vmcnt<0>();
-            __syncthreads();
+        int slab = 0;
+        for (; slab + S <= nk; slab += S) {
+            step(ic<0>{}, slab);
+            step(ic<1>{}, slab + 1);
+            if constexpr (S > 2) step(ic<2 % S>{}, slab + 2);
+            if constexpr (S > 3) step(ic<3 % S>{}, slab + 3);
         }
-        if (ks + 1 < nk) {  // two slabs left
-            issue(stage1, (ks + 1) * BK);
-            compute(stage0);
-            wait_vmcnt<0>();
-            __syncthreads();
-            compute(stage1);
-        } else {            // one slab left
-            compute(stage0);
-        }
+        if (slab < nk) step(ic<0>{}, slab++);
+        if constexpr (S > 2) if (slab < nk) step(ic<1 % S>{}, slab++);
+        if constexpr (S > 3) if (slab < nk) step(ic<2 % S>{}, slab++);
+        wait_vmcnt<0>();  // the trailing prefetches must land before the LDS is reused
         __syncthreads();
 
         // epilogue: activation on the fp32 accumulator, RNE to bf16, 8-byte stores
@@ -232,18 +240,17 @@ struct Bf16Body {
 };
 
 // ----------------------------------------------------------------------------
-// fp32 tile body (64 x 64, BK = 32) on v_mfma_f32_32x32x2_f32.  Small chains
-// only; A is transposed into LDS ([k][m], padded) so that both fragment reads
-// are lane-contiguous.
+// fp32 tile body (64 x 64, BK = 32) on v_mfma_f32_32x32x2_f32, two stages,
+// register-staged.  Small chains only; A is transposed into LDS ([k][m],
+// padded) so that both fragment reads are lane-contiguous.
 // ----------------------------------------------------------------------------
 struct F32Body {
-    static constexpr int BM = 64, BN = 64, BK = 32;
+    static constexpr int BM = 64, BN = 64, BK = 32, S = 2;
     static constexpr int AP = BM + 1;  // padded A row ([k][m])
     static constexpr int BP = BN + 4;  // padded W row ([k][n]), keeps 16-byte alignment
     static constexpr int STAGE = (BK * AP + BK * BP) * 4;
 
-    __device__ __forceinline__ static void run(const LayerDesc &d, int i, int j, char *stage0,
-                                               char *stage1) {
+    __device__ __forceinline__ static void run(const LayerDesc &d, int i, int j, char *const *stg) {
         const float *__restrict__ A = static_cast<const float *>(d.A);
         const float *__restrict__ W = static_cast<const float *>(d.W);
         float *__restrict__ C = static_cast<float *>(d.C);
@@ -266,8 +273,8 @@ struct F32Body {
                 rb[q] = *reinterpret_cast<const float4 *>(W + (size_t)(k0 + k) * N + col0 + n4 * 4);
             }
         };
-        auto lstore = [&](int buf) {
-            float *As = reinterpret_cast<float *>(buf ? stage1 : stage0);
+        auto lstore = [&](char *st) {
+            float *As = reinterpret_cast<float *>(st);
             float *Bs = As + BK * AP;
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
@@ -280,8 +287,8 @@ struct F32Body {
                 *reinterpret_cast<float4 *>(Bs + k * BP + n4 * 4) = rb[q];
             }
         };
-        auto compute = [&](int buf) {
-            const float *As = reinterpret_cast<const float *>(buf ? stage1 : stage0);
+        auto compute = [&](const char *st) {
+            const float *As = reinterpret_cast<const float *>(st);
             const float *Bs = As + BK * AP;
 #pragma unroll
             for (int kk = 0; kk < BK / 2; ++kk) {
@@ -294,12 +301,12 @@ struct F32Body {
 
         const int nk = K / BK;
         gload(0);
-        lstore(0);
+        lstore(stg[0]);
         __syncthreads();
         for (int ks = 0; ks < nk; ++ks) {
             if (ks + 1 < nk) gload((ks + 1) * BK);
-            compute(ks & 1);
-            if (ks + 1 < nk) lstore((ks + 1) & 1);
+            compute(stg[ks & 1]);
+            if (ks + 1 < nk) lstore(stg[(ks + 1) & 1]);
             __syncthreads();
         }
 
@@ -316,6 +323,37 @@ struct F32Body {
     }
 };
 
+// LDS stages of a body: one __shared__ array per stage (see Bf16Body).
+template <class Body, int S = Body::S>
+struct Stages;
+template <class Body>
+struct Stages<Body, 2> {
+    __device__ __forceinline__ static void get(char **p) {
+        __shared__ __attribute__((aligned(1024))) char s0[Body::STAGE];
+        __shared__ __attribute__((aligned(1024))) char s1[Body::STAGE];
+        p[0] = s0; p[1] = s1; p[2] = s0; p[3] = s1;
+    }
+};
+template <class Body>
+struct Stages<Body, 3> {
+    __device__ __forceinline__ static void get(char **p) {
+        __shared__ __attribute__((aligned(1024))) char s0[Body::STAGE];
+        __shared__ __attribute__((aligned(1024))) char s1[Body::STAGE];
+        __shared__ __attribute__((aligned(1024))) char s2[Body::STAGE];
+        p[0] = s0; p[1] = s1; p[2] = s2; p[3] = s0;
+    }
+};
+template <class Body>
+struct Stages<Body, 4> {
+    __device__ __forceinline__ static void get(char **p) {
+        __shared__ __attribute__((aligned(1024))) char s0[Body::STAGE];
+        __shared__ __attribute__((aligned(1024))) char s1[Body::STAGE];
+        __shared__ __attribute__((aligned(1024))) char s2[Body::STAGE];
+        __shared__ __attribute__((aligned(1024))) char s3[Body::STAGE];
+        p[0] = s0; p[1] = s1; p[2] = s2; p[3] = s3;
+    }
+};
+
 // ----------------------------------------------------------------------------
 // Protocol: prologue (consumer side) and publish (producer side).
 // ----------------------------------------------------------------------------
@@ -323,21 +361,28 @@ __device__ __forceinline__ uint32_t ld_relaxed(const uint32_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Thread 0 only.  Take the next queue slot (ticket), wait until a tile ID has
-// been pushed into it, and make the producers' stores of that tile's inputs
-// visible.  Returns the tile ID, or kDone when the queue is exhausted or the
-// run has failed.  Slots are handed out in order, so a waiting worker only
-// ever waits on tiles held by workers that took earlier slots and are
-// already running: the wait always ends for a well-formed dependency table.
-__device__ uint32_t prologue(const ChainArgs &a) {
+// Thread 0 only.  Take the next slot (ticket) of this worker's queue q, wait
+// until a tile ID has been pushed into it, and make the producers' stores of
+// that tile's inputs visible.  Returns the tile ID, or kDone when the queue
+// is exhausted or the run has failed.
+//
+// Forward progress: slots of a queue are handed out in order and pushes
+// claim slots in order, so if some tile is ready, every slot of its queue
+// below it is claimed and filled without waiting.  Take an unfinished tile
+// of lowest layer: its producers are finished, so it has been pushed, and
+// the workers of its queue reach it.  Every queue has workers and all
+// workers are co-resident (cooperative launch), so no wait lasts forever
+// for a well-formed dependency table.
+__device__ uint32_t prologue(const ChainArgs &a, int q) {
     if (ld_relaxed(a.ctl + kCtlStatus) != 0) return kDone;
-    const uint32_t t = __hip_atomic_fetch_add(a.ctl + kCtlHead, 1u, __ATOMIC_RELAXED,
+    const uint32_t t = __hip_atomic_fetch_add(a.ctl + ctl_head(q), 1u, __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_AGENT);
-    if (t >= (uint32_t)a.T) return kDone;
+    if (t >= (uint32_t)a.qsize[q]) return kDone;
+    const uint32_t *slot = a.queue + a.qbase[q] + t;
     const uint64_t t0 = wall_clock64();
     uint32_t id;
     uint32_t polls = 0;
-    while ((id = ld_relaxed(a.queue + t)) == kEmpty) {
+    while ((id = ld_relaxed(slot)) == kEmpty) {
         __builtin_amdgcn_s_sleep(1);
         if ((++polls & 63) == 0) {
             if (wall_clock64() - t0 > a.timeout_ticks) {
@@ -363,43 +408,49 @@ __device__ uint32_t prologue(const ChainArgs &a) {
     return id;
 }
 
-// All threads.  Called after the tile's stores.  Each wave releases its own
-// stores at agent scope (write-back of this XCD's L2) before the barrier; then
-// wave 0 decrements the counter of every consumer, one edge per lane, and
-// pushes the consumers whose counter reached zero with one atomic on the tail.
-__device__ void publish(const ChainArgs &a, uint32_t id) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+// All threads.  Called after the tile's stores.  The barrier makes every
+// wave's stores happen-before wave 0's agent-scope release (write-back of
+// this XCD's L2); wave 0 then decrements the counter of every consumer (all
+// in layer l+1), one edge per lane, and pushes the consumers whose counter
+// reached zero into their owner queues, one tail atomic per queue.
+__device__ void publish(const ChainArgs &a, uint32_t id, int l) {
     __syncthreads();
     const int tid = threadIdx.x;
     if (tid >= 64) return;
     const int lane = tid;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     if ((a.flags & CP_FLAG_DELAY_INJECT) && ((id * 2654435761u) >> 30) == 0) {
         const uint64_t s = wall_clock64();
         while (wall_clock64() - s < 2000) __builtin_amdgcn_s_sleep(8);  // ~20 us
     }
     if (a.trace && lane == 0) a.trace[4 * (size_t)id + 3] = wall_clock64();
+    const LayerDesc &next = a.layer[l + 1];
     const int beg = a.dep_off[id], end = a.dep_off[id + 1];
     for (int e0 = beg; e0 < end; e0 += 64) {
         const int e = e0 + lane;
         bool ready = false;
         uint32_t c = 0;
+        int cq = 0;
         if (e < end) {
             c = (uint32_t)a.dep_ids[e];
             const int old = __hip_atomic_fetch_sub(a.score + c, 1, __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_AGENT);
             ready = (old == 1);
+            cq = owner_queue(next, (int)c, a.nq);
         }
-        const uint64_t mask = __ballot(ready);
-        if (mask) {
+        if (!__ballot(ready)) continue;
+        for (int q = 0; q < a.nq; ++q) {
+            const uint64_t mask = __ballot(ready && cq == q);
+            if (!mask) continue;
             const int leader = __ffsll((unsigned long long)mask) - 1;
             uint32_t base = 0;
             if (lane == leader)
-                base = __hip_atomic_fetch_add(a.ctl + kCtlTail, (uint32_t)__popcll(mask),
+                base = __hip_atomic_fetch_add(a.ctl + ctl_tail(q), (uint32_t)__popcll(mask),
                                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             base = __shfl(base, leader);
-            if (ready) {
+            if (ready && cq == q) {
                 const uint32_t rank = (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
-                __hip_atomic_store(a.queue + base + rank, c, __ATOMIC_RELAXED,
+                __hip_atomic_store(a.queue + a.qbase[q] + base + rank, c, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
             }
         }
@@ -418,26 +469,30 @@ __device__ __forceinline__ void decode(const ChainArgs &a, uint32_t id, int &l, 
 // Kernels
 // ----------------------------------------------------------------------------
 
-// Persistent worker: loop prologue -> tile body -> publish until the queue is
-// exhausted.  Grid = number of workers (<= co-resident workgroups).
+// Persistent worker: loop prologue -> tile body -> publish until its queue
+// (blockIdx.x mod nq, so that workgroups dispatched round-robin over the
+// XCDs serve the queue of their own XCD) is exhausted.  Launched
+// cooperatively: all workers are co-resident.  The tile ID is broadcast
+// through the first word of stage 0; the second barrier guarantees every
+// thread has read it before the body's loads reuse stage 0.
 template <class Body>
 __global__ void __launch_bounds__(kThreads) worker_kernel(ChainArgs a) {
-    __shared__ __attribute__((aligned(1024))) char stage0[Body::STAGE];
-    __shared__ __attribute__((aligned(1024))) char stage1[Body::STAGE];
-    __shared__ uint32_t s_id;
+    char *stg[4];
+    Stages<Body>::get(stg);
+    volatile uint32_t *slot = reinterpret_cast<volatile uint32_t *>(stg[0]);
+    const int q = (int)(blockIdx.x % (unsigned)a.nq);
     for (;;) {
-        if (threadIdx.x == 0) s_id = prologue(a);
+        if (threadIdx.x == 0) *slot = prologue(a, q);
         __syncthreads();
-        const uint32_t id = s_id;
+        const uint32_t id = *slot;
+        __syncthreads();
         if (id >= (uint32_t)a.T) break;
         int l, i, j;
         decode(a, id, l, i, j);
-        Body::run(a.layer[l], i, j, stage0, stage1);
+        Body::run(a.layer[l], i, j, stg);
         if (a.trace && threadIdx.x == 0) a.trace[4 * (size_t)id + 2] = wall_clock64();
-        if (l + 1 < a.L) {
-            publish(a, id);
-        }
-        __syncthreads();  // s_id is rewritten by the next prologue
+        if (l + 1 < a.L) publish(a, id, l);
+        __syncthreads();
     }
 }
 
@@ -445,21 +500,22 @@ __global__ void __launch_bounds__(kThreads) worker_kernel(ChainArgs a) {
 // kernel-boundary execution used by the sequential and micro-batched modes.
 template <class Body>
 __global__ void __launch_bounds__(kThreads) layer_kernel(ChainArgs a, int l, int rb0) {
-    __shared__ __attribute__((aligned(1024))) char stage0[Body::STAGE];
-    __shared__ __attribute__((aligned(1024))) char stage1[Body::STAGE];
+    char *stg[4];
+    Stages<Body>::get(stg);
     const LayerDesc &d = a.layer[l];
     const int t = blockIdx.x;
     const int i = rb0 + t / d.nbn, j = t % d.nbn;
-    Body::run(d, i, j, stage0, stage1);
+    Body::run(d, i, j, stg);
 }
 
-// Per-run state reset: scoreboard from the in-degree template, queue
-// pre-filled with the first layer's tiles (row-block-major) and EMPTY after.
-__global__ void reset_kernel(ChainArgs a, int n_first) {
+// Per-run state reset: scoreboard from the in-degree template, queues from
+// their initial image (each pre-filled with its first-layer tiles in
+// row-block-major order, EMPTY after), per-queue head = 0, tail = pre-filled.
+__global__ void reset_kernel(ChainArgs a) {
     const int stride = gridDim.x * blockDim.x;
     for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < a.T; t += stride) {
         a.score[t] = a.indeg[t];
-        a.queue[t] = t < n_first ? (uint32_t)t : kEmpty;
+        a.queue[t] = a.qinit[t];
         if (a.deq_count) a.deq_count[t] = 0;
         if (a.trace) {
             a.trace[4 * (size_t)t + 0] = 0;
@@ -468,10 +524,11 @@ __global__ void reset_kernel(ChainArgs a, int n_first) {
             a.trace[4 * (size_t)t + 3] = 0;
         }
     }
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-        a.ctl[kCtlHead] = 0;
-        a.ctl[kCtlTail] = (uint32_t)n_first;
-        a.ctl[kCtlStatus] = 0;
+    if (blockIdx.x == 0 && threadIdx.x < kMaxQueues) {
+        const int q = threadIdx.x;
+        a.ctl[ctl_head(q)] = 0;
+        a.ctl[ctl_tail(q)] = q < a.nq ? (uint32_t)a.qfirst[q] : 0u;
+        if (q == 0) a.ctl[kCtlStatus] = 0;
     }
 }
 
@@ -486,9 +543,15 @@ __global__ void poison_kernel(uint32_t *p, size_t words, uint32_t pattern) {
 // Launchers and the variant table
 // ----------------------------------------------------------------------------
 template <class Body>
-hipError_t launch_worker_t(const ChainArgs &a, int grid, hipStream_t s) {
-    hipLaunchKernelGGL(worker_kernel<Body>, dim3(grid), dim3(kThreads), 0, s, a);
-    return hipGetLastError();
+hipError_t launch_worker_t(const ChainArgs &a, int grid, bool cooperative, hipStream_t s) {
+    if (!cooperative) {
+        hipLaunchKernelGGL(worker_kernel<Body>, dim3(grid), dim3(kThreads), 0, s, a);
+        return hipGetLastError();
+    }
+    ChainArgs copy = a;
+    void *args[] = {&copy};
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(worker_kernel<Body>), dim3(grid),
+                                      dim3(kThreads), args, 0, s);
 }
 
 template <class Body>
@@ -504,9 +567,39 @@ hipError_t occupancy_t(int *blocks) {
     return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, worker_kernel<Body>, kThreads, 0);
 }
 
-#define CP_BF16_VARIANT(bm, bn)                                                                 \
-    {CP_BF16, bm, bn, 64, 2 * Bf16Body<bm, bn>::STAGE, launch_worker_t<Bf16Body<bm, bn>>,          \
-     launch_layer_t<Bf16Body<bm, bn>>, occupancy_t<Bf16Body<bm, bn>>}
+// LDS stages per tile shape: as many as fit the occupancy each shape aims for
+#ifndef CP_S_256x256
+#define CP_S_256x256 2
+#endif
+#ifndef CP_S_256x128
+#define CP_S_256x128 3
+#endif
+#ifndef CP_S_128x256
+#define CP_S_128x256 3
+#endif
+#ifndef CP_S_128x128
+#define CP_S_128x128 2
+#endif
+#ifndef CP_S_256x64
+#define CP_S_256x64 2
+#endif
+#ifndef CP_S_64x256
+#define CP_S_64x256 2
+#endif
+#ifndef CP_S_128x64
+#define CP_S_128x64 3
+#endif
+#ifndef CP_S_64x128
+#define CP_S_64x128 3
+#endif
+#ifndef CP_S_64x64
+#define CP_S_64x64 4
+#endif
+
+#define CP_BF16_VARIANT(bm, bn)                                                            \
+    {CP_BF16, bm, bn, 64, CP_S_##bm##x##bn * Bf16Body<bm, bn, CP_S_##bm##x##bn>::STAGE,    \
+     launch_worker_t<Bf16Body<bm, bn, CP_S_##bm##x##bn>>,                                 \
+     launch_layer_t<Bf16Body<bm, bn, CP_S_##bm##x##bn>>, occupancy_t<Bf16Body<bm, bn, CP_S_##bm##x##bn>>}
 
 static const Variant kVariants[] = {
     {CP_F32, 64, 64, 32, 2 * F32Body::STAGE, launch_worker_t<F32Body>, launch_layer_t<F32Body>,
@@ -527,11 +620,11 @@ const Variant *variant_list(int *count) {
     return kVariants;
 }
 
-hipError_t launch_reset(const ChainArgs &a, int n_first, hipStream_t s) {
+hipError_t launch_reset(const ChainArgs &a, hipStream_t s) {
     int grid = (a.T + kThreads - 1) / kThreads;
     if (grid > 1024) grid = 1024;
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL(reset_kernel, dim3(grid), dim3(kThreads), 0, s, a, n_first);
+    hipLaunchKernelGGL(reset_kernel, dim3(grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 

@@ -42,6 +42,7 @@ class cp_chain_stats_t(ctypes.Structure):
         ("tile_m", ctypes.c_int32), ("tile_n", ctypes.c_int32),
         ("nonzero_scores", ctypes.c_int32), ("bad_dequeues", ctypes.c_int32),
         ("queue_is_perm", ctypes.c_int32), ("head", ctypes.c_uint32), ("tail", ctypes.c_uint32),
+        ("n_queues", ctypes.c_int32), ("queues_drained", ctypes.c_int32),
         ("order_violations", ctypes.c_int32), ("last_run_ms", ctypes.c_double),
         ("last_kernel_ms", ctypes.c_double),
     ]
