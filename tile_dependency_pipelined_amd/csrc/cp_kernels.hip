@@ -73,10 +73,15 @@ using ic = std::integral_constant<int, U>;
 // store instructions are needed; the swizzle below is applied by choosing
 // which global 16-byte chunk each lane fetches.
 //   A tile [BM][64] bf16, 128-byte rows, chunk c of row r stored at chunk
-//     position c ^ (r & 7): the MFMA A fragment (8 consecutive k of one row)
-//     is one ds_read_b128, 8 consecutive rows hit 8 distinct bank groups.
+//     position c ^ fa(r), fa(r) = (r ^ (r >> 3)) & 7: the MFMA A fragment (8
+//     consecutive k of one row) is one ds_read_b128; 8 consecutive rows hit 8
+//     distinct 16-byte bank groups of a 128-byte window, and 16 consecutive
+//     rows 16 distinct groups of a 256-byte window.
 //   W tile [64][BN] bf16 in its natural n-contiguous layout, chunk c of row k
-//     stored at c ^ 2 (k & 3).  The B fragment (8 consecutive k of one column)
+//     stored at c ^ fb(k), fb = {0, 6, 10, 12}[k mod 4] (BN >= 128): the 4
+//     rows x 2 chunks read by 16 lanes are distinct modulo 128 bytes and the
+//     4 rows x 4 chunks read by 32 lanes distinct modulo 256 bytes.
+//     The B fragment (8 consecutive k of one column)
 //     is read by two ds_read_b64_tr_b16: within a group of 16 lanes, result
 //     lane i, element j is element (i mod 4) of the 8 bytes addressed by lane
 //     4 j + i / 4, so lane s addresses row k0 + s/4, columns n0 + 4 (s mod 4)
@@ -103,7 +108,11 @@ struct Bf16Body {
     static_assert(A_PW >= 1 && B_PW >= 1, "loads per wave");
     static_assert(S >= 2 && S <= 4 && (S - 2) * PER < 64, "stages");
 
-    __device__ static int fb(int k) { return (k & 3) << 1; }
+    __device__ static int fa(int r) { return (r ^ (r >> 3)) & 7; }
+    __device__ static int fb(int k) {
+        if constexpr (BN >= 128) return (0xCA60 >> ((k & 3) * 4)) & 15;  // 0, 6, 10, 12
+        else return (k & 3) << 1;
+    }
 
     __device__ __forceinline__ static void run(const LayerDesc &d, int i, int j, char *const *stg) {
         const uint16_t *__restrict__ A = static_cast<const uint16_t *>(d.A);
@@ -128,7 +137,7 @@ struct Bf16Body {
 #pragma unroll
         for (int q = 0; q < A_PW; ++q) {
             const int o = (q * 4 + wave) * 1024 + lane * 16;  // byte in the A region
-            const int r = o >> 7, c = ((o >> 4) & 7) ^ (r & 7);
+            const int r = o >> 7, c = ((o >> 4) & 7) ^ fa(r);
             a_off[q] = (uint32_t)((row0 + r) * K + c * 8);
         }
 #pragma unroll
@@ -155,38 +164,70 @@ struct Bf16Body {
         const int g = lane >> 5;                  // k half of the fragment
         const int s4 = (lane & 15) >> 2;          // row within a transpose group
         const int nb = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-        auto compute = [&](const char *As) {
+        // fragments of one k step (16 k) of the wave's sub-tile
+        struct Frags {
+            bf16x8_t a[FM], b[FN];
+        };
+        auto load = [&](const char *As, int kk, Frags &f) {
             const char *Bs = As + A_BYTES;
+            const int c = kk * 2 + g;
 #pragma unroll
-            for (int kk = 0; kk < BK / 16; ++kk) {
-                const int c = kk * 2 + g;
-                bf16x8_t af[FM], bfv[FN];
-#pragma unroll
-                for (int fm = 0; fm < FM; ++fm) {
-                    const int r = wm * WM + fm * 32 + (lane & 31);
-                    af[fm] = *reinterpret_cast<const bf16x8_t *>(As + r * 128 + ((c ^ (r & 7)) << 4));
-                }
-#pragma unroll
-                for (int fn = 0; fn < FN; ++fn) {
-                    const int n = wn * WN + fn * 32 + nb;
-                    const int k = kk * 16 + 8 * g + s4;
-                    const int cn = n >> 3, half = ((n >> 2) & 1) * 8;
-                    const char *p0 = Bs + k * RB + ((cn ^ fb(k)) << 4) + half;
-                    const char *p1 = Bs + (k + 4) * RB + ((cn ^ fb(k + 4)) << 4) + half;
-                    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)p0);
-                    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)p1);
-                    const v4i16_t both[2] = {lo, hi};
-                    bfv[fn] = *reinterpret_cast<const bf16x8_t *>(both);
-                }
-                // W fragment as the first operand: the result holds, per lane,
-                // output row m = lane%32 and four consecutive output columns.
-#pragma unroll
-                for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-                    for (int fn = 0; fn < FN; ++fn)
-                        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfv[fn], af[fm],
-                                                                              acc[fm][fn], 0, 0, 0);
+            for (int fm = 0; fm < FM; ++fm) {
+                const int r = wm * WM + fm * 32 + (lane & 31);
+                f.a[fm] = *reinterpret_cast<const bf16x8_t *>(As + r * 128 + ((c ^ fa(r)) << 4));
             }
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const int n = wn * WN + fn * 32 + nb;
+                const int k = kk * 16 + 8 * g + s4;
+                const int cn = n >> 3, half = ((n >> 2) & 1) * 8;
+                const char *p0 = Bs + k * RB + ((cn ^ fb(k)) << 4) + half;
+                const char *p1 = Bs + (k + 4) * RB + ((cn ^ fb(k + 4)) << 4) + half;
+                const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)p0);
+                const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t *)p1);
+                const v4i16_t both[2] = {lo, hi};
+                f.b[fn] = *reinterpret_cast<const bf16x8_t *>(both);
+            }
+        };
+        // W fragment as the first operand: the result holds, per lane, output
+        // row m = lane%32 and four consecutive output columns.
+        auto mma = [&](const Frags &f) {
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[fn], f.a[fm], acc[fm][fn],
+                                                                          0, 0, 0);
+        };
+        // One slab: the reads of k step kk+1 are issued between the MFMAs of
+        // k step kk, so that LDS latency hides behind matrix work.  The
+        // scheduling barriers pin that interleaving (the compiler would
+        // otherwise group each step's reads right before its own MFMAs).
+        constexpr int KS = BK / 16;                // k steps per slab
+        constexpr int RD = FM + 2 * FN;            // LDS reads per k step
+        constexpr int MF = FM * FN;                // MFMAs per k step
+        auto compute = [&](const char *As) {
+            Frags f[2];
+            load(As, 0, f[0]);
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                if (kk + 1 < KS) load(As, kk + 1, f[(kk + 1) & 1]);
+                mma(f[kk & 1]);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x020, PER, 0);  // the slab prefetch, first
+            __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);   // reads of step 0
+            constexpr int PAIRS = RD < MF ? RD : MF;
+#pragma unroll
+            for (int kk = 0; kk + 1 < KS; ++kk) {
+#pragma unroll
+                for (int r = 0; r < PAIRS; ++r) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one read of step kk+1
+                }
+                if constexpr (RD > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, RD - PAIRS, 0);
+                if constexpr (MF > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, MF - PAIRS, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);  // last step
         };
 
         const int nk = K / BK;
