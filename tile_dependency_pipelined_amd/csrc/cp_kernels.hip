@@ -93,19 +93,23 @@ using ic = std::integral_constant<int, U>;
 // slab the prefetch re-reads the last slab into a stage that is never used,
 // which keeps the number of loads in flight, and so the wait, constant.
 // ----------------------------------------------------------------------------
-template <int BM_, int BN_, int S_>
+template <int BM_, int BN_, int S_, int WGM_ = 2, int WGN_ = 2>
 struct Bf16Body {
     static constexpr int BM = BM_, BN = BN_, BK = 64, S = S_;
-    static constexpr int WM = BM / 2, WN = BN / 2;   // per-wave sub-tile (2 x 2 waves)
+    static constexpr int WGM = WGM_, WGN = WGN_;     // wave grid
+    static constexpr int NW = WGM * WGN, NT = 64 * NW;
+    static constexpr int WM = BM / WGM, WN = BN / WGN;  // per-wave sub-tile
     static constexpr int FM = WM / 32, FN = WN / 32; // 32x32 MFMA blocks per wave
     static constexpr int RB = BN * 2;                // bytes per W row in LDS
     static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * RB;
-    static constexpr int A_PW = A_BYTES / 1024 / 4;  // 1 KiB direct loads per wave (A)
-    static constexpr int B_PW = B_BYTES / 1024 / 4;  // (W)
+    static constexpr int A_PW = A_BYTES / 1024 / NW;  // 1 KiB direct loads per wave (A)
+    static constexpr int B_PW = B_BYTES / 1024 / NW;  // (W)
     static constexpr int PER = A_PW + B_PW;          // loads per wave per slab
     static constexpr int STAGE = A_BYTES + B_BYTES;  // bytes of one LDS stage
     static_assert(BM >= 64 && BN >= 64 && BM <= 256 && BN <= 256, "tile");
-    static_assert(A_PW >= 1 && B_PW >= 1, "loads per wave");
+    static_assert(WM >= 32 && WN >= 32 && WM % 32 == 0 && WN % 32 == 0, "wave sub-tile");
+    static_assert(A_PW >= 1 && B_PW >= 1 && A_PW * NW * 1024 == A_BYTES && B_PW * NW * 1024 == B_BYTES,
+                  "loads per wave");
     static_assert(S >= 2 && S <= 4 && (S - 2) * PER < 64, "stages");
 
     __device__ static int fa(int r) { return (r ^ (r >> 3)) & 7; }
@@ -122,7 +126,7 @@ struct Bf16Body {
         const int row0 = i * BM, col0 = j * BN;
         const int tid = threadIdx.x, lane = tid & 63;
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-        const int wm = wave >> 1, wn = wave & 1;
+        const int wm = wave / WGN, wn = wave % WGN;
 
         f32x16_t acc[FM][FN];
 #pragma unroll
@@ -136,13 +140,13 @@ struct Bf16Body {
         uint32_t a_off[A_PW], b_off[B_PW];
 #pragma unroll
         for (int q = 0; q < A_PW; ++q) {
-            const int o = (q * 4 + wave) * 1024 + lane * 16;  // byte in the A region
+            const int o = (q * NW + wave) * 1024 + lane * 16;  // byte in the A region
             const int r = o >> 7, c = ((o >> 4) & 7) ^ fa(r);
             a_off[q] = (uint32_t)((row0 + r) * K + c * 8);
         }
 #pragma unroll
         for (int q = 0; q < B_PW; ++q) {
-            const int o = (q * 4 + wave) * 1024 + lane * 16;  // byte in the W region
+            const int o = (q * NW + wave) * 1024 + lane * 16;  // byte in the W region
             const int k = o / RB, c = ((o % RB) >> 4) ^ fb(o / RB);
             b_off[q] = (uint32_t)(k * N + col0 + c * 8);
         }
@@ -152,12 +156,12 @@ struct Bf16Body {
 #pragma unroll
             for (int q = 0; q < A_PW; ++q)
                 __builtin_amdgcn_global_load_lds(A + a_off[q] + k0,
-                                                 (lds_void_t *)(As + (q * 4 + wave) * 1024), 16, 0, 0);
+                                                 (lds_void_t *)(As + (q * NW + wave) * 1024), 16, 0, 0);
             const uint16_t *Wk = W + (size_t)k0 * N;
 #pragma unroll
             for (int q = 0; q < B_PW; ++q)
                 __builtin_amdgcn_global_load_lds(Wk + b_off[q],
-                                                 (lds_void_t *)(Bs + (q * 4 + wave) * 1024), 16, 0, 0);
+                                                 (lds_void_t *)(Bs + (q * NW + wave) * 1024), 16, 0, 0);
         };
 
         // fragment addresses that do not depend on the stage or k step
@@ -286,7 +290,7 @@ struct Bf16Body {
 // padded) so that both fragment reads are lane-contiguous.
 // ----------------------------------------------------------------------------
 struct F32Body {
-    static constexpr int BM = 64, BN = 64, BK = 32, S = 2;
+    static constexpr int BM = 64, BN = 64, BK = 32, S = 2, NT = 256;
     static constexpr int AP = BM + 1;  // padded A row ([k][m])
     static constexpr int BP = BN + 4;  // padded W row ([k][n]), keeps 16-byte alignment
     static constexpr int STAGE = (BK * AP + BK * BP) * 4;
@@ -517,7 +521,7 @@ __device__ __forceinline__ void decode(const ChainArgs &a, uint32_t id, int &l, 
 // through the first word of stage 0; the second barrier guarantees every
 // thread has read it before the body's loads reuse stage 0.
 template <class Body>
-__global__ void __launch_bounds__(kThreads) worker_kernel(ChainArgs a) {
+__global__ void __launch_bounds__(Body::NT) worker_kernel(ChainArgs a) {
     char *stg[4];
     Stages<Body>::get(stg);
     volatile uint32_t *slot = reinterpret_cast<volatile uint32_t *>(stg[0]);
@@ -540,7 +544,7 @@ __global__ void __launch_bounds__(kThreads) worker_kernel(ChainArgs a) {
 // One layer, one tile per workgroup, row-blocks [rb0, rb0 + nrb): the plain
 // kernel-boundary execution used by the sequential and micro-batched modes.
 template <class Body>
-__global__ void __launch_bounds__(kThreads) layer_kernel(ChainArgs a, int l, int rb0) {
+__global__ void __launch_bounds__(Body::NT) layer_kernel(ChainArgs a, int l, int rb0) {
     char *stg[4];
     Stages<Body>::get(stg);
     const LayerDesc &d = a.layer[l];
@@ -586,26 +590,26 @@ __global__ void poison_kernel(uint32_t *p, size_t words, uint32_t pattern) {
 template <class Body>
 hipError_t launch_worker_t(const ChainArgs &a, int grid, bool cooperative, hipStream_t s) {
     if (!cooperative) {
-        hipLaunchKernelGGL(worker_kernel<Body>, dim3(grid), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL(worker_kernel<Body>, dim3(grid), dim3(Body::NT), 0, s, a);
         return hipGetLastError();
     }
     ChainArgs copy = a;
     void *args[] = {&copy};
     return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(worker_kernel<Body>), dim3(grid),
-                                      dim3(kThreads), args, 0, s);
+                                      dim3(Body::NT), args, 0, s);
 }
 
 template <class Body>
 hipError_t launch_layer_t(const ChainArgs &a, int l, int rb0, int nrb, hipStream_t s) {
     const int grid = nrb * a.layer[l].nbn;
     if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL(layer_kernel<Body>, dim3(grid), dim3(kThreads), 0, s, a, l, rb0);
+    hipLaunchKernelGGL(layer_kernel<Body>, dim3(grid), dim3(Body::NT), 0, s, a, l, rb0);
     return hipGetLastError();
 }
 
 template <class Body>
 hipError_t occupancy_t(int *blocks) {
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, worker_kernel<Body>, kThreads, 0);
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, worker_kernel<Body>, Body::NT, 0);
 }
 
 // LDS stages per tile shape: as many as fit the occupancy each shape aims for
@@ -637,10 +641,39 @@ hipError_t occupancy_t(int *blocks) {
 #define CP_S_64x64 4
 #endif
 
-#define CP_BF16_VARIANT(bm, bn)                                                            \
-    {CP_BF16, bm, bn, 64, CP_S_##bm##x##bn * Bf16Body<bm, bn, CP_S_##bm##x##bn>::STAGE,    \
-     launch_worker_t<Bf16Body<bm, bn, CP_S_##bm##x##bn>>,                                 \
-     launch_layer_t<Bf16Body<bm, bn, CP_S_##bm##x##bn>>, occupancy_t<Bf16Body<bm, bn, CP_S_##bm##x##bn>>}
+// wave grid (waves along M x along N) per tile shape
+#ifndef CP_W_256x256
+#define CP_W_256x256 2, 4
+#endif
+#ifndef CP_W_256x128
+#define CP_W_256x128 2, 2
+#endif
+#ifndef CP_W_128x256
+#define CP_W_128x256 2, 2
+#endif
+#ifndef CP_W_128x128
+#define CP_W_128x128 2, 2
+#endif
+#ifndef CP_W_256x64
+#define CP_W_256x64 2, 2
+#endif
+#ifndef CP_W_64x256
+#define CP_W_64x256 2, 2
+#endif
+#ifndef CP_W_128x64
+#define CP_W_128x64 2, 2
+#endif
+#ifndef CP_W_64x128
+#define CP_W_64x128 2, 2
+#endif
+#ifndef CP_W_64x64
+#define CP_W_64x64 2, 2
+#endif
+
+#define CP_BODY(bm, bn) Bf16Body<bm, bn, CP_S_##bm##x##bn, CP_W_##bm##x##bn>
+#define CP_BF16_VARIANT(bm, bn)                                                                  \
+    {CP_BF16, bm, bn, 64, CP_S_##bm##x##bn * CP_BODY(bm, bn)::STAGE,                            \
+     launch_worker_t<CP_BODY(bm, bn)>, launch_layer_t<CP_BODY(bm, bn)>, occupancy_t<CP_BODY(bm, bn)>}
 
 static const Variant kVariants[] = {
     {CP_F32, 64, 64, 32, 2 * F32Body::STAGE, launch_worker_t<F32Body>, launch_layer_t<F32Body>,
