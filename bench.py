@@ -165,7 +165,7 @@ def main():
         "bound": bound, "achieved": round(kernel_tflops, 2), "peak": peak, "unit": "TFLOP/s",
         "frac": round(kernel_tflops / peak, 4),
         "traffic": traffic,
-        "kernel": "cp::worker_kernel<Bf16Body<%d,%d>>" % tile if cfg.dtype == gen.BF16 else "worker_kernel<F32Body>",
+        "kernel": "cp::worker_kernel<Bf16Body<%d,%d,...>>" % tile if cfg.dtype == gen.BF16 else "worker_kernel<F32Body>",
         "kernel_us": round(kernel_ms * 1e3, 1),
         "algorithmic_flop_per_launch": flops,
         "algorithmic_bytes_min": cfg.min_bytes(),

@@ -2,17 +2,29 @@
 counter dumps into the short text summaries kept under profiles/, and read
 back the HBM traffic figure the benchmark reports.
 
-Traffic summaries are named traffic_<workload>_<bm>x<bn>.txt and hold
-`key: value` lines, among them the SHA-256 of the kernel source they were
-taken on; a summary taken on another kernel source is ignored (traffic null).
+    python -m tile_dependency_pipelined_amd.profiling summarize \
+        --workload c3 --tile 256x256 --stats <kernel_stats.csv> \
+        --fetch <counter_collection.csv> --write <counter_collection.csv> \
+        --cmd "<the commands that made the inputs>" --out profiles/<name>.md
+
+Traffic: FETCH_SIZE and WRITE_SIZE (KiB per dispatch, from two separate
+--pmc runs) of the persistent worker kernel, each scaled by the factor that
+maps the same counter of a plain 1 GiB device copy (torch's copy kernel,
+reading 1 GiB and writing 1 GiB) onto its known size.  A summary records the
+SHA-256 of the kernel source it was taken on; a summary taken on another
+kernel source is ignored (traffic null).
 """
+import argparse
 import csv
-import glob
 import hashlib
 import os
+import statistics
+import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = [os.path.join(PKG, "csrc", "cp_kernels.hip"), os.path.join(PKG, "csrc", "cp_device.h")]
+COPY_BYTES = 1 << 30
+WORKER = "worker_kernel"
 
 
 def kernel_source_sha256() -> str:
@@ -27,14 +39,19 @@ def parse_kv(path):
     out = {}
     with open(path) as f:
         for line in f:
+            line = line.strip().lstrip("-* ")
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
-                out[k.strip()] = v.strip()
+                out[k.strip().strip("`")] = v.strip().strip("`")
     return out
 
 
+def traffic_path(profiles_dir, workload, tile):
+    return os.path.join(profiles_dir, f"worker_{workload}_{tile[0]}x{tile[1]}.md")
+
+
 def load_traffic(profiles_dir, workload, tile):
-    path = os.path.join(profiles_dir, f"traffic_{workload}_{tile[0]}x{tile[1]}.txt")
+    path = traffic_path(profiles_dir, workload, tile)
     if not os.path.exists(path):
         return None
     kv = parse_kv(path)
@@ -46,27 +63,117 @@ def load_traffic(profiles_dir, workload, tile):
         return None
 
 
-def read_counter_csv(path):
-    """Rows of a rocprofv3 counter_collection.csv as dicts."""
+def read_csv(path):
     with open(path, newline="") as f:
         return list(csv.DictReader(f))
 
 
-def counter_per_dispatch(rows, kernel_substr, counter):
-    """{dispatch_id: summed counter value} for dispatches whose kernel name
-    contains kernel_substr."""
+def _get(r, *names):
+    for n in names:
+        if n in r and r[n] != "":
+            return r[n]
+    return None
+
+
+def counter_per_dispatch(rows, match, counter):
+    """{dispatch_id: value} of `counter` for dispatches whose kernel name
+    satisfies match(name)."""
     acc = {}
     for r in rows:
-        name = r.get("Kernel_Name") or r.get("Kernel-Name") or ""
-        if kernel_substr not in name:
+        name = _get(r, "Kernel_Name", "Kernel-Name") or ""
+        if not match(name):
             continue
-        if (r.get("Counter_Name") or r.get("Counter-Name")) != counter:
+        if _get(r, "Counter_Name", "Counter-Name") != counter:
             continue
-        d = r.get("Dispatch_Id") or r.get("Dispatch-Id")
-        acc[d] = acc.get(d, 0.0) + float(r.get("Counter_Value") or r.get("Counter-Value") or 0)
+        d = _get(r, "Dispatch_Id", "Dispatch-Id")
+        acc[d] = acc.get(d, 0.0) + float(_get(r, "Counter_Value", "Counter-Value") or 0)
     return acc
 
 
-def find_one(pattern):
-    hits = sorted(glob.glob(pattern, recursive=True))
-    return hits[-1] if hits else None
+def is_copy(name):
+    return "copy" in name.lower() and WORKER not in name
+
+
+def kernel_stats(path):
+    """Rows of a rocprofv3 kernel_stats.csv: name, calls, average ns."""
+    out = []
+    for r in read_csv(path):
+        name = _get(r, "Name", "KernelName", "Kernel_Name")
+        calls = _get(r, "Calls")
+        avg = _get(r, "AverageNs", "Average_ns", "AverageNs(ns)")
+        if name is None or avg is None:
+            continue
+        out.append((name, int(float(calls or 0)), float(avg)))
+    return out
+
+
+def summarize(args):
+    lines = [f"# rocprofv3 summary: persistent worker kernel, workload {args.workload}, "
+             f"tile {args.tile}", ""]
+    lines.append("Commands (run from the repository root on the GPU box):")
+    lines.append("")
+    for c in args.cmd:
+        lines.append(f"    {c}")
+    lines.append("")
+    kv = {"workload": args.workload, "tile": args.tile,
+          "kernel_source_sha256": kernel_source_sha256()}
+    if args.stats:
+        st = kernel_stats(args.stats)
+        lines.append("Kernel statistics (rocprofv3 --kernel-trace --stats):")
+        lines.append("")
+        lines.append("| kernel | calls | average us |")
+        lines.append("|---|---|---|")
+        for name, calls, avg in sorted(st, key=lambda x: -x[1] * x[2])[:8]:
+            short = name if len(name) < 90 else name[:87] + "..."
+            lines.append(f"| `{short}` | {calls} | {avg / 1e3:.1f} |")
+        lines.append("")
+        w = [s for s in st if WORKER in s[0]]
+        if w:
+            kv["worker_average_us"] = f"{w[0][2] / 1e3:.1f}"
+    for tag, path, counter in (("fetch", args.fetch, "FETCH_SIZE"), ("write", args.write, "WRITE_SIZE")):
+        if not path:
+            continue
+        rows = read_csv(path)
+        wk = counter_per_dispatch(rows, lambda n: WORKER in n, counter)
+        cp = counter_per_dispatch(rows, is_copy, counter)
+        if not wk or not cp:
+            lines.append(f"{counter}: worker or copy dispatches missing in {os.path.basename(path)}")
+            continue
+        w_kib = statistics.median(wk.values())
+        # the 1 GiB calibration copies are the largest copy dispatches
+        c_kib = statistics.median(sorted(cp.values())[-3:])
+        scale = (COPY_BYTES / 1024.0) / c_kib if c_kib > 0 else float("nan")
+        kv[f"{tag}_kib_per_launch_raw"] = f"{w_kib:.0f}"
+        kv[f"{tag}_copy_kib_raw"] = f"{c_kib:.0f}"
+        kv[f"{tag}_scale"] = f"{scale:.4f}"
+        kv[f"{tag}_bytes_per_launch"] = f"{w_kib * 1024 * scale:.0f}"
+    if "fetch_bytes_per_launch" in kv and "write_bytes_per_launch" in kv:
+        kv["hbm_bytes_per_launch"] = str(int(float(kv["fetch_bytes_per_launch"]) +
+                                             float(kv["write_bytes_per_launch"])))
+    lines.append("Figures (key: value):")
+    lines.append("")
+    for k, v in kv.items():
+        lines.append(f"- {k}: {v}")
+    lines.append("")
+    with open(args.out, "w") as f:
+        f.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmdname", required=True)
+    s = sub.add_parser("summarize")
+    s.add_argument("--workload", required=True)
+    s.add_argument("--tile", required=True)
+    s.add_argument("--stats")
+    s.add_argument("--fetch")
+    s.add_argument("--write")
+    s.add_argument("--cmd", action="append", default=[])
+    s.add_argument("--out", required=True)
+    args = ap.parse_args(argv)
+    summarize(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -7,8 +7,8 @@ TILES = {
     "c1": (64, 64),
     "c2": (128, 128),
     "c3": (256, 256),
-    "c4": (256, 256),
-    "c5": (64, 256),
+    "c4": (256, 128),
+    "c5": (128, 128),
 }
 
 # rows per chunk swept by the micro-batched baseline (each a multiple of tile_m
