@@ -65,18 +65,20 @@ template <int U>
 using ic = std::integral_constant<int, U>;
 
 // ----------------------------------------------------------------------------
-// bf16 tile body: C[BM x BN] tile (i, j) of A[M][K] . W[K][N], BK = 64,
-// S-stage LDS pipeline.
+// bf16 tile body: C[BM x BN] tile (i, j) of A[M][K] . W[K][N], slabs of BK
+// (32 or 64) k, S-stage LDS pipeline.
 //
 // Both operands travel HBM -> LDS by 16-byte direct loads (global_load_lds):
 // lane l of a load lands at LDS base + 16 l, so no VGPR staging and no LDS
 // store instructions are needed; the swizzle below is applied by choosing
 // which global 16-byte chunk each lane fetches.
-//   A tile [BM][64] bf16, 128-byte rows, chunk c of row r stored at chunk
-//     position c ^ fa(r), fa(r) = (r ^ (r >> 3)) & 7: the MFMA A fragment (8
-//     consecutive k of one row) is one ds_read_b128; 8 consecutive rows hit 8
-//     distinct 16-byte bank groups of a 128-byte window, and 16 consecutive
-//     rows 16 distinct groups of a 256-byte window.
+//   A tile [BM][BK] bf16.  BK = 64: 128-byte rows, chunk c of row r stored at
+//     chunk position c ^ fa(r), fa(r) = (r ^ (r >> 3)) & 7.  BK = 32: rows
+//     2L and 2L+1 share the 128-byte line L, chunk c of row r at position
+//     (4 (r & 1) + c) ^ fl(L), fl(L) = (L ^ (L >> 2)) & 3.  Either way the
+//     MFMA A fragment (8 consecutive k of one row) is one ds_read_b128, 8
+//     consecutive rows hit 8 distinct 16-byte bank groups of a 128-byte
+//     window, and 16 consecutive rows 16 distinct groups of a 256-byte window.
 //   W tile [64][BN] bf16 in its natural n-contiguous layout, chunk c of row k
 //     stored at c ^ fb(k), fb = {0, 6, 10, 12}[k mod 4] (BN >= 128): the 4
 //     rows x 2 chunks read by 16 lanes are distinct modulo 128 bytes and the
@@ -86,16 +88,18 @@ using ic = std::integral_constant<int, U>;
 //     lane i, element j is element (i mod 4) of the 8 bytes addressed by lane
 //     4 j + i / 4, so lane s addresses row k0 + s/4, columns n0 + 4 (s mod 4)
 //     and lane i receives W[k0 .. k0+3][n0 + i].
-// Pipeline: S-1 slabs are in flight while one is multiplied.  Every stage is
-// its own __shared__ array and every stage index a compile-time constant, so
-// the compiler can tell that loads in flight into one stage do not alias
-// reads of another and does not wait for them before reading.  Past the last
-// slab the prefetch re-reads the last slab into a stage that is never used,
-// which keeps the number of loads in flight, and so the wait, constant.
+// Pipeline: S-1 slabs are in flight while one is multiplied; a stage is
+// refilled as soon as every wave holds the fragments of its last k step.
+// Every stage is its own __shared__ array and every stage index a
+// compile-time constant, so the compiler can tell that loads in flight into
+// one stage do not alias reads of another and does not wait for them before
+// reading.  Past the last slab the prefetch re-reads the last slab into a
+// stage that is no longer read, which keeps the number of loads in flight,
+// and so the wait, constant.
 // ----------------------------------------------------------------------------
-template <int BM_, int BN_, int S_, int WGM_ = 2, int WGN_ = 2>
+template <int BM_, int BN_, int S_, int WGM_ = 2, int WGN_ = 2, int BK_ = 64>
 struct Bf16Body {
-    static constexpr int BM = BM_, BN = BN_, BK = 64, S = S_;
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_;
     static constexpr int WGM = WGM_, WGN = WGN_;     // wave grid
     static constexpr int NW = WGM * WGN, NT = 64 * NW;
     static constexpr int WM = BM / WGM, WN = BN / WGN;  // per-wave sub-tile
@@ -110,9 +114,17 @@ struct Bf16Body {
     static_assert(WM >= 32 && WN >= 32 && WM % 32 == 0 && WN % 32 == 0, "wave sub-tile");
     static_assert(A_PW >= 1 && B_PW >= 1 && A_PW * NW * 1024 == A_BYTES && B_PW * NW * 1024 == B_BYTES,
                   "loads per wave");
-    static_assert(S >= 2 && S <= 4 && (S - 2) * PER < 64, "stages");
+    static_assert(BK == 32 || BK == 64, "k slab");
+    static_assert(S >= 2 && S <= 5 && (S - 1) * PER < 64, "stages");
 
-    __device__ static int fa(int r) { return (r ^ (r >> 3)) & 7; }
+    // byte offset of 16-byte chunk c (0 .. BK/8-1) of A row r within the A tile
+    __device__ static int a_at(int r, int c) {
+        if constexpr (BK == 64) return r * 128 + ((c ^ ((r ^ (r >> 3)) & 7)) << 4);
+        else {
+            const int L = r >> 1;
+            return L * 128 + ((((r & 1) << 2 | c) ^ ((L ^ (L >> 2)) & 3)) << 4);
+        }
+    }
     __device__ static int fb(int k) {
         if constexpr (BN >= 128) return (0xCA60 >> ((k & 3) * 4)) & 15;  // 0, 6, 10, 12
         else return (k & 3) << 1;
@@ -141,7 +153,15 @@ struct Bf16Body {
 #pragma unroll
         for (int q = 0; q < A_PW; ++q) {
             const int o = (q * NW + wave) * 1024 + lane * 16;  // byte in the A region
-            const int r = o >> 7, c = ((o >> 4) & 7) ^ fa(r);
+            int r, c;
+            if constexpr (BK == 64) {
+                r = o >> 7;
+                c = ((o >> 4) & 7) ^ ((r ^ (r >> 3)) & 7);
+            } else {  // inverse of a_at for 64-byte rows
+                const int L = o >> 7, v = ((o >> 4) & 7) ^ ((L ^ (L >> 2)) & 3);
+                r = 2 * L + (v >> 2);
+                c = v & 3;
+            }
             a_off[q] = (uint32_t)((row0 + r) * K + c * 8);
         }
 #pragma unroll
@@ -178,7 +198,7 @@ struct Bf16Body {
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm) {
                 const int r = wm * WM + fm * 32 + (lane & 31);
-                f.a[fm] = *reinterpret_cast<const bf16x8_t *>(As + r * 128 + ((c ^ fa(r)) << 4));
+                f.a[fm] = *reinterpret_cast<const bf16x8_t *>(As + a_at(r, c));
             }
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
@@ -203,23 +223,26 @@ struct Bf16Body {
                     acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[fn], f.a[fm], acc[fm][fn],
                                                                           0, 0, 0);
         };
-        // One slab: the reads of k step kk+1 are issued between the MFMAs of
-        // k step kk, so that LDS latency hides behind matrix work.  The
-        // scheduling barriers pin that interleaving (the compiler would
-        // otherwise group each step's reads right before its own MFMAs).
+        // Software pipeline over k steps that crosses slab boundaries: the
+        // fragment reads of k step kk+1 are issued between the MFMAs of k step
+        // kk, including the reads of the next slab's first step, which ride on
+        // the MFMAs of this slab's last step.  The workgroup barrier therefore
+        // sits before that last step: by then every wave has read all of this
+        // slab (its last-step fragments are in registers), so the stage can be
+        // refilled, and the next slab has landed.  The scheduling barriers pin
+        // the interleaving (the compiler would otherwise group each step's
+        // reads right before its own MFMAs).
         constexpr int KS = BK / 16;                // k steps per slab
         constexpr int RD = FM + 2 * FN;            // LDS reads per k step
         constexpr int MF = FM * FN;                // MFMAs per k step
-        auto compute = [&](const char *As) {
-            Frags f[2];
-            load(As, 0, f[0]);
+        static_assert(KS % 2 == 0, "fragment double buffer parity");
+        Frags f[2];
+        auto head = [&](const char *As) {          // k steps 0 .. KS-2 of a slab
 #pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                if (kk + 1 < KS) load(As, kk + 1, f[(kk + 1) & 1]);
+            for (int kk = 0; kk + 1 < KS; ++kk) {
+                load(As, kk + 1, f[(kk + 1) & 1]);
                 mma(f[kk & 1]);
             }
-            __builtin_amdgcn_sched_group_barrier(0x020, PER, 0);  // the slab prefetch, first
-            __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);   // reads of step 0
             constexpr int PAIRS = RD < MF ? RD : MF;
 #pragma unroll
             for (int kk = 0; kk + 1 < KS; ++kk) {
@@ -231,34 +254,51 @@ struct Bf16Body {
                 if constexpr (RD > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, RD - PAIRS, 0);
                 if constexpr (MF > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, MF - PAIRS, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);  // last step
+        };
+        // last k step of a slab, the refill of its stage and the first reads
+        // of the next slab, interleaved MFMA / read / direct load
+        auto tail = [&](char *refill, int k0, const char *Anext) {
+            issue(refill, k0);
+            load(Anext, 0, f[0]);
+            mma(f[(KS - 1) & 1]);
+            constexpr int R = MF > RD ? (MF > PER ? MF : PER) : (RD > PER ? RD : PER);
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                if (r < MF) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (r < RD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (r < PER) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
         };
 
         const int nk = K / BK;
-        // one pipeline step: prefetch slab+S-1 into the stage freed last step,
-        // multiply slab, wait until slab+1 has landed, publish it to all waves
+        // one pipeline step on the slab in stage u: slabs slab+1 .. slab+S-1
+        // are in flight into the other stages; after the barrier stage u is
+        // refilled with slab+S
         auto step = [&](auto U, int slab) {
             constexpr int u = decltype(U)::value;
-            const int pre = slab + S - 1 < nk ? slab + S - 1 : nk - 1;
-            issue(stg[(u + S - 1) % S], pre * BK);
-            compute(stg[u]);
+            head(stg[u]);
             wait_vmcnt<(S - 2) * PER>();
             __syncthreads();
+            const int pre = slab + S < nk ? slab + S : nk - 1;
+            tail(stg[u], pre * BK, stg[(u + 1) % S]);
         };
 #pragma unroll
-        for (int u = 0; u < S - 1; ++u) issue(stg[u], (u < nk ? u : nk - 1) * BK);
-        wait_vmcnt<(S - 2) * PER>();
+        for (int u = 0; u < S; ++u) issue(stg[u], (u < nk ? u : nk - 1) * BK);
+        wait_vmcnt<(S - 1) * PER>();
         __syncthreads();
+        load(stg[0], 0, f[0]);
         int slab = 0;
         for (; slab + S <= nk; slab += S) {
             step(ic<0>{}, slab);
             step(ic<1>{}, slab + 1);
             if constexpr (S > 2) step(ic<2 % S>{}, slab + 2);
             if constexpr (S > 3) step(ic<3 % S>{}, slab + 3);
+            if constexpr (S > 4) step(ic<4 % S>{}, slab + 4);
         }
         if (slab < nk) step(ic<0>{}, slab++);
         if constexpr (S > 2) if (slab < nk) step(ic<1 % S>{}, slab++);
         if constexpr (S > 3) if (slab < nk) step(ic<2 % S>{}, slab++);
+        if constexpr (S > 4) if (slab < nk) step(ic<3 % S>{}, slab++);
         wait_vmcnt<0>();  // the trailing prefetches must land before the LDS is reused
         __syncthreads();
 
@@ -376,7 +416,7 @@ struct Stages<Body, 2> {
     __device__ __forceinline__ static void get(char **p) {
         __shared__ __attribute__((aligned(1024))) char s0[Body::STAGE];
         __shared__ __attribute__((aligned(1024))) char s1[Body::STAGE];
-        p[0] = s0; p[1] = s1; p[2] = s0; p[3] = s1;
+        p[0] = s0; p[1] = s1; p[2] = s0; p[3] = s1; p[4] = s0;
     }
 };
 template <class Body>
@@ -385,7 +425,18 @@ struct Stages<Body, 3> {
         __shared__ __attribute__((aligned(1024))) char s0[Body::STAGE];
         __shared__ __attribute__((aligned(1024))) char s1[Body::STAGE];
         __shared__ __attribute__((aligned(1024))) char s2[Body::STAGE];
-        p[0] = s0; p[1] = s1; p[2] = s2; p[3] = s0;
+        p[0] = s0; p[1] = s1; p[2] = s2; p[3] = s0; p[4] = s1;
+    }
+};
+template <class Body>
+struct Stages<Body, 5> {
+    __device__ __forceinline__ static void get(char **p) {
+        __shared__ __attribute__((aligned(1024))) char s0[Body::STAGE];
+        __shared__ __attribute__((aligned(1024))) char s1[Body::STAGE];
+        __shared__ __attribute__((aligned(1024))) char s2[Body::STAGE];
+        __shared__ __attribute__((aligned(1024))) char s3[Body::STAGE];
+        __shared__ __attribute__((aligned(1024))) char s4[Body::STAGE];
+        p[0] = s0; p[1] = s1; p[2] = s2; p[3] = s3; p[4] = s4;
     }
 };
 template <class Body>
@@ -395,7 +446,7 @@ struct Stages<Body, 4> {
         __shared__ __attribute__((aligned(1024))) char s1[Body::STAGE];
         __shared__ __attribute__((aligned(1024))) char s2[Body::STAGE];
         __shared__ __attribute__((aligned(1024))) char s3[Body::STAGE];
-        p[0] = s0; p[1] = s1; p[2] = s2; p[3] = s3;
+        p[0] = s0; p[1] = s1; p[2] = s2; p[3] = s3; p[4] = s0;
     }
 };
 
@@ -522,7 +573,7 @@ __device__ __forceinline__ void decode(const ChainArgs &a, uint32_t id, int &l, 
 // thread has read it before the body's loads reuse stage 0.
 template <class Body>
 __global__ void __launch_bounds__(Body::NT) worker_kernel(ChainArgs a) {
-    char *stg[4];
+    char *stg[5];
     Stages<Body>::get(stg);
     volatile uint32_t *slot = reinterpret_cast<volatile uint32_t *>(stg[0]);
     const int q = (int)(blockIdx.x % (unsigned)a.nq);
@@ -545,7 +596,7 @@ __global__ void __launch_bounds__(Body::NT) worker_kernel(ChainArgs a) {
 // kernel-boundary execution used by the sequential and micro-batched modes.
 template <class Body>
 __global__ void __launch_bounds__(Body::NT) layer_kernel(ChainArgs a, int l, int rb0) {
-    char *stg[4];
+    char *stg[5];
     Stages<Body>::get(stg);
     const LayerDesc &d = a.layer[l];
     const int t = blockIdx.x;
@@ -670,9 +721,38 @@ hipError_t occupancy_t(int *blocks) {
 #define CP_W_64x64 2, 2
 #endif
 
-#define CP_BODY(bm, bn) Bf16Body<bm, bn, CP_S_##bm##x##bn, CP_W_##bm##x##bn>
+// k slab per tile shape
+#ifndef CP_K_256x256
+#define CP_K_256x256 64
+#endif
+#ifndef CP_K_256x128
+#define CP_K_256x128 64
+#endif
+#ifndef CP_K_128x256
+#define CP_K_128x256 64
+#endif
+#ifndef CP_K_128x128
+#define CP_K_128x128 64
+#endif
+#ifndef CP_K_256x64
+#define CP_K_256x64 64
+#endif
+#ifndef CP_K_64x256
+#define CP_K_64x256 64
+#endif
+#ifndef CP_K_128x64
+#define CP_K_128x64 64
+#endif
+#ifndef CP_K_64x128
+#define CP_K_64x128 64
+#endif
+#ifndef CP_K_64x64
+#define CP_K_64x64 64
+#endif
+
+#define CP_BODY(bm, bn) Bf16Body<bm, bn, CP_S_##bm##x##bn, CP_W_##bm##x##bn, CP_K_##bm##x##bn>
 #define CP_BF16_VARIANT(bm, bn)                                                                  \
-    {CP_BF16, bm, bn, 64, CP_S_##bm##x##bn * CP_BODY(bm, bn)::STAGE,                            \
+    {CP_BF16, bm, bn, CP_K_##bm##x##bn, CP_S_##bm##x##bn * CP_BODY(bm, bn)::STAGE,                            \
      launch_worker_t<CP_BODY(bm, bn)>, launch_layer_t<CP_BODY(bm, bn)>, occupancy_t<CP_BODY(bm, bn)>}
 
 static const Variant kVariants[] = {
