@@ -75,6 +75,16 @@ typedef struct cp_chain cp_chain; /* opaque plan */
  * becomes ready; the worker holding its slot gives up after 50 ms (instead of
  * the default 2 s), sets CP_ERR_TIMEOUT and every worker exits.  Needs L >= 2. */
 #define CP_FLAG_STARVE_LAST 16u
+/* sequential and micro-batched modes: launch kernel by kernel instead of
+ * replaying the plan's cached hipGraph of the run */
+#define CP_FLAG_EAGER 32u
+/* pipelined mode: launch the worker grid cooperatively, so that the runtime
+ * guarantees every worker is resident even on a device shared with other
+ * work; without it the grid (sized to what the device holds at once) is a
+ * plain launch, which skips the cooperative launch path's extra latency and
+ * relies on the device being otherwise idle (else the watchdog may end the
+ * run with CP_ERR_TIMEOUT) */
+#define CP_FLAG_COOPERATIVE 64u
 
 #define CP_MAX_LAYERS 8
 
@@ -131,9 +141,20 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
  *   microbatch_rows   CP_MODE_MICROBATCH only: rows per chunk, a multiple of
  *                     tile_m dividing M (the static micro-batching baseline's
  *                     "chunk size", §IV-A); ignored otherwise
- * Pipelined mode resets the scoreboard/queue on the stream, then launches one
- * persistent grid.  At most one run may be in flight per plan.  A device-side
- * watchdog expiry is reported by cp_chain_stats (status CP_ERR_TIMEOUT).
+ * Pipelined mode launches one persistent grid.  The plan holds two copies of
+ * the per-run scoreboard/queue state; a run uses one and its workers reset
+ * the other for the next run, so no reset launch precedes the grid.  The
+ * sequential and micro-batched baselines are captured
+ * once per (mode, microbatch_rows, X, W, Y) into a hipGraph that the plan owns
+ * (at most 16 are kept, least recently used dropped) and replayed with one
+ * hipGraphLaunch, as the paper's baselines replay CUDA graphs (§IV-A); with
+ * CP_FLAG_EAGER their kernels are enqueued one by one.  While `stream` is
+ * itself being captured, a sequential or micro-batched run is recorded kernel
+ * by kernel into the caller's graph and is not timed (cp_chain_stats keeps
+ * reporting the last uncaptured run); pipelined mode returns
+ * CP_ERR_UNSUPPORTED there (a replay would reuse one state copy).  At most one run may be in flight per plan.  A
+ * device-side watchdog expiry is reported by cp_chain_stats (status
+ * CP_ERR_TIMEOUT).
  */
 int cp_chain_run(cp_chain *plan, const void *X, const void *const *W, void *Y,
                  void *stream, int32_t mode, int64_t microbatch_rows);

@@ -201,6 +201,21 @@ def test_many_tiles_many_waves(rt):
     assert same_bits(out["pipelined"], out["sequential"])
 
 
+@pytest.mark.parametrize("coop", [False, True], ids=["plain", "cooperative"])
+def test_pipelined_repeats_alternate_state(rt, coop):
+    """Back-to-back pipelined runs alternate between the plan's two copies of
+    the scoreboard/queue state, each reset by the previous run's workers:
+    every run must meet the invariants and give the same bits."""
+    nat = rt["nat"]
+    M, widths = 512, (256, 512, 256)
+    X, Ws = gen.chain_inputs(M, widths, gen.BF16, 1.0, (1 / 16, 1 / np.sqrt(512)), 83)
+    flags = all_flags() | (nat.CP_FLAG_COOPERATIVE if coop else 0)
+    say("alternating state copies, cooperative" if coop else "alternating state copies, plain launch")
+    out, st = run_modes(rt, X, Ws, gen.BF16, (64, 64), flags=flags, modes=("pipelined",), reps=5)
+    ref = oracle.chain(X, Ws, gen.BF16)
+    assert oracle.rel_err(as_values(out["pipelined"], gen.BF16), ref) <= TOL[gen.BF16]
+
+
 def test_rejects_bad_shapes_on_device(rt):
     nat = rt["nat"]
     with pytest.raises(nat.CpError) as e:
@@ -222,6 +237,12 @@ def test_watchdog_timeout_is_reported(rt):
         say("watchdog stats", st)
         assert st["rc"] == nat.CP_ERR_TIMEOUT and st["status"] == nat.CP_ERR_TIMEOUT
         assert st["tail"] == st["n_tiles"] - 1 and st["queues_drained"] == 0
+        # the failed run still reset the other state copy: a second run fails
+        # the same way, not earlier or later
+        c.run(dX, dW, dY)
+        st = c.stats(check=False)
+        assert st["status"] == nat.CP_ERR_TIMEOUT and st["tail"] == st["n_tiles"] - 1, st
+        assert st["bad_dequeues"] == 1, st   # only the starved tile is never dequeued
         # the plan is reusable afterwards in the other modes
         c.run(dX, dW, dY, mode="sequential")
         assert c.stats()["status"] == 0

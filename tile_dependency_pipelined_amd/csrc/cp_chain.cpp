@@ -121,16 +121,34 @@ struct cp_chain {
     int n_workers = 0;
     int nq = 1;                        // work-queues (one per XCD, at most kMaxQueues)
     int32_t qbase[cp::kMaxQueues] = {}, qsize[cp::kMaxQueues] = {}, qfirst[cp::kMaxQueues] = {};
-    bool coop = true;                  // cooperative launch of the persistent grid
-    // device state (one allocation) and intermediates
+    bool coop = false;                 // cooperative launch of the persistent grid
+    // device state (one allocation) and intermediates.  The per-run state
+    // (scoreboard, queues, counters, debug counts, trace) has two copies: a
+    // pipelined run uses copy `cur` and its workers reset the other one,
+    // which the next run uses, so no reset launch precedes the worker grid.
     char *state = nullptr;
-    int32_t *d_score = nullptr, *d_indeg = nullptr, *d_dep_off = nullptr, *d_dep_ids = nullptr;
-    uint32_t *d_queue = nullptr, *d_ctl = nullptr, *d_deq = nullptr, *d_qinit = nullptr;
-    uint64_t *d_trace = nullptr;
+    int32_t *d_indeg = nullptr, *d_dep_off = nullptr, *d_dep_ids = nullptr;
+    uint32_t *d_qinit = nullptr;
+    int32_t *d_score[2] = {};
+    uint32_t *d_queue[2] = {}, *d_ctl[2] = {}, *d_deq[2] = {};
+    uint64_t *d_trace[2] = {};
+    int cur = 0;                       // copy of the next pipelined run
+    int last_copy = 0;                 // copy of the last pipelined run
     void *inter[CP_MAX_LAYERS] = {};
     size_t inter_bytes[CP_MAX_LAYERS] = {};
     hipStream_t side[2] = {nullptr, nullptr};
+    hipStream_t cap = nullptr;         // origin stream of graph captures
     hipEvent_t ev_fork = nullptr, ev_join[2] = {nullptr, nullptr};
+    // replayable sequential / micro-batched runs, keyed by mode, chunk and pointers
+    struct Replay {
+        int32_t mode = 0;
+        int64_t mb = 0;
+        const void *X = nullptr, *W[CP_MAX_LAYERS] = {};
+        void *Y = nullptr;
+        hipGraph_t graph = nullptr;
+        hipGraphExec_t exec = nullptr;
+    };
+    std::vector<Replay> replays;       // most recently used last
     hipEvent_t ev_start = nullptr, ev_kernel = nullptr, ev_stop = nullptr;
     uint64_t timeout_ticks = 200000000ull;  // 2 s at 100 MHz
     int32_t last_mode = -1;
@@ -139,10 +157,21 @@ struct cp_chain {
 
 namespace {
 
+constexpr size_t kMaxReplays = 16;
+
+void drop_replay(cp_chain::Replay &r) {
+    if (r.exec) (void)hipGraphExecDestroy(r.exec);
+    if (r.graph) (void)hipGraphDestroy(r.graph);
+    r.exec = nullptr;
+    r.graph = nullptr;
+}
+
 void release(cp_chain *p) {
     if (!p) return;
+    for (auto &r : p->replays) drop_replay(r);
     for (auto &s : p->side)
         if (s) (void)hipStreamDestroy(s);
+    if (p->cap) (void)hipStreamDestroy(p->cap);
     if (p->ev_fork) (void)hipEventDestroy(p->ev_fork);
     for (auto &e : p->ev_join)
         if (e) (void)hipEventDestroy(e);
@@ -157,7 +186,7 @@ void release(cp_chain *p) {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-cp::ChainArgs make_args(const cp_chain *p, const void *X, const void *const *W, void *Y) {
+cp::ChainArgs make_args(const cp_chain *p, const void *X, const void *const *W, void *Y, int copy) {
     cp::ChainArgs a;
     memset(&a, 0, sizeof a);
     const size_t es = p->dtype == CP_BF16 ? 2 : 4;
@@ -165,7 +194,7 @@ cp::ChainArgs make_args(const cp_chain *p, const void *X, const void *const *W, 
     for (int l = 0; l < p->L; ++l) {
         cp::LayerDesc &d = a.layer[l];
         d.A = l == 0 ? X : p->inter[l - 1];
-        d.W = W[l];
+        d.W = W ? W[l] : nullptr;
         d.C = l + 1 == p->L ? Y : p->inter[l];
         d.K = (int32_t)p->widths[l];
         d.N = (int32_t)p->widths[l + 1];
@@ -184,14 +213,20 @@ cp::ChainArgs make_args(const cp_chain *p, const void *X, const void *const *W, 
         a.qfirst[q] = p->qfirst[q];
     }
     a.qinit = p->d_qinit;
-    a.queue = p->d_queue;
-    a.ctl = p->d_ctl;
-    a.score = p->d_score;
+    const int c = copy, n = copy ^ 1;
+    a.queue = p->d_queue[c];
+    a.ctl = p->d_ctl[c];
+    a.score = p->d_score[c];
+    a.nxt_queue = p->d_queue[n];
+    a.nxt_ctl = p->d_ctl[n];
+    a.nxt_score = p->d_score[n];
     a.dep_off = p->d_dep_off;
     a.dep_ids = p->d_dep_ids;
     a.indeg = p->d_indeg;
-    a.deq_count = (p->flags & CP_FLAG_DEBUG) ? p->d_deq : nullptr;
-    a.trace = (p->flags & CP_FLAG_TRACE) ? p->d_trace : nullptr;
+    a.deq_count = (p->flags & CP_FLAG_DEBUG) ? p->d_deq[c] : nullptr;
+    a.trace = (p->flags & CP_FLAG_TRACE) ? p->d_trace[c] : nullptr;
+    a.nxt_deq_count = (p->flags & CP_FLAG_DEBUG) ? p->d_deq[n] : nullptr;
+    a.nxt_trace = (p->flags & CP_FLAG_TRACE) ? p->d_trace[n] : nullptr;
     a.timeout_ticks = p->timeout_ticks;
     return a;
 }
@@ -255,7 +290,8 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
         for (int l = 0; l < n_layers; ++l)
             if (acts[l] != CP_ACT_NONE && acts[l] != CP_ACT_GELU_TANH)
                 return fail(CP_ERR_INVALID_ARG, "acts[%d] = %d", l, acts[l]);
-    const uint32_t known = CP_FLAG_DEBUG | CP_FLAG_TRACE | CP_FLAG_POISON | CP_FLAG_DELAY_INJECT | CP_FLAG_STARVE_LAST;
+    const uint32_t known = CP_FLAG_DEBUG | CP_FLAG_TRACE | CP_FLAG_POISON | CP_FLAG_DELAY_INJECT | CP_FLAG_STARVE_LAST |
+                           CP_FLAG_EAGER | CP_FLAG_COOPERATIVE;
     if (flags & ~known) return fail(CP_ERR_INVALID_ARG, "unknown flags 0x%x", flags & ~known);
     if ((flags & CP_FLAG_STARVE_LAST) && n_layers < 2)
         return fail(CP_ERR_INVALID_ARG, "CP_FLAG_STARVE_LAST needs at least two layers");
@@ -293,26 +329,31 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
     // one device allocation for all protocol state
     const size_t T = (size_t)g.T, E = (size_t)std::max(g.E, 1);
     size_t off = 0;
-    const size_t o_ctl = off;     off = align_up(off + cp::kCtlWords * 4, 256);
-    const size_t o_score = off;   off = align_up(off + T * 4, 256);
-    const size_t o_queue = off;   off = align_up(off + T * 4, 256);
+    size_t o_ctl[2], o_score[2], o_queue[2], o_deq[2], o_trace[2];
+    for (int c = 0; c < 2; ++c) {
+        o_ctl[c] = off;   off = align_up(off + cp::kCtlWords * 4, 256);
+        o_score[c] = off; off = align_up(off + T * 4, 256);
+        o_queue[c] = off; off = align_up(off + T * 4, 256);
+        o_deq[c] = off;   off = align_up(off + T * 4, 256);
+        o_trace[c] = off; off = align_up(off + ((flags & CP_FLAG_TRACE) ? T * 32 : 0), 256);
+    }
     const size_t o_indeg = off;   off = align_up(off + T * 4, 256);
     const size_t o_doff = off;    off = align_up(off + (T + 1) * 4, 256);
     const size_t o_dids = off;    off = align_up(off + E * 4, 256);
-    const size_t o_deq = off;     off = align_up(off + T * 4, 256);
     const size_t o_qinit = off;   off = align_up(off + T * 4, 256);
-    const size_t o_trace = off;   off = align_up(off + ((flags & CP_FLAG_TRACE) ? T * 32 : 0), 256);
     int rc2 = [&]() -> int {
         CP_HIP(hipMalloc(&p->state, off));
-        p->d_ctl = reinterpret_cast<uint32_t *>(p->state + o_ctl);
-        p->d_score = reinterpret_cast<int32_t *>(p->state + o_score);
-        p->d_queue = reinterpret_cast<uint32_t *>(p->state + o_queue);
+        for (int c = 0; c < 2; ++c) {
+            p->d_ctl[c] = reinterpret_cast<uint32_t *>(p->state + o_ctl[c]);
+            p->d_score[c] = reinterpret_cast<int32_t *>(p->state + o_score[c]);
+            p->d_queue[c] = reinterpret_cast<uint32_t *>(p->state + o_queue[c]);
+            p->d_deq[c] = reinterpret_cast<uint32_t *>(p->state + o_deq[c]);
+            p->d_trace[c] = (flags & CP_FLAG_TRACE) ? reinterpret_cast<uint64_t *>(p->state + o_trace[c]) : nullptr;
+        }
         p->d_indeg = reinterpret_cast<int32_t *>(p->state + o_indeg);
         p->d_dep_off = reinterpret_cast<int32_t *>(p->state + o_doff);
         p->d_dep_ids = reinterpret_cast<int32_t *>(p->state + o_dids);
-        p->d_deq = reinterpret_cast<uint32_t *>(p->state + o_deq);
         p->d_qinit = reinterpret_cast<uint32_t *>(p->state + o_qinit);
-        p->d_trace = (flags & CP_FLAG_TRACE) ? reinterpret_cast<uint64_t *>(p->state + o_trace) : nullptr;
         CP_HIP(hipMemset(p->state, 0, off));
         CP_HIP(hipMemcpy(p->d_indeg, g.indeg.data(), T * 4, hipMemcpyHostToDevice));
         CP_HIP(hipMemcpy(p->d_dep_off, g.dep_off.data(), (T + 1) * 4, hipMemcpyHostToDevice));
@@ -323,6 +364,7 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
             CP_HIP(hipMalloc(&p->inter[l], p->inter_bytes[l]));
         }
         for (auto &s : p->side) CP_HIP(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
+        CP_HIP(hipStreamCreateWithFlags(&p->cap, hipStreamNonBlocking));
         CP_HIP(hipEventCreateWithFlags(&p->ev_fork, hipEventDisableTiming));
         for (auto &e : p->ev_join) CP_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
         CP_HIP(hipEventCreate(&p->ev_start));
@@ -333,10 +375,13 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
         CP_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device));
         if (per_cu < 1) return fail(CP_ERR_UNSUPPORTED, "kernel cannot be resident (occupancy 0)");
         p->n_workers = std::max(1, std::min(per_cu * cus, g.T));
-        int coop_ok = 0;
-        if (hipDeviceGetAttribute(&coop_ok, hipDeviceAttributeCooperativeLaunch, p->device) != hipSuccess)
-            coop_ok = 0;
-        p->coop = coop_ok != 0;
+        if (flags & CP_FLAG_COOPERATIVE) {
+            int coop_ok = 0;
+            if (hipDeviceGetAttribute(&coop_ok, hipDeviceAttributeCooperativeLaunch, p->device) != hipSuccess)
+                coop_ok = 0;
+            if (!coop_ok) return fail(CP_ERR_UNSUPPORTED, "device has no cooperative launch");
+            p->coop = true;
+        }
         // one queue per XCD; a tile belongs to the queue of its column panel
         int xcds = 8;
         p->nq = std::max(1, std::min({cp::kMaxQueues, xcds, p->n_workers}));
@@ -358,6 +403,9 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
             base += size[q];
         }
         CP_HIP(hipMemcpy(p->d_qinit, qinit.data(), T * 4, hipMemcpyHostToDevice));
+        // both copies of the per-run state start reset
+        for (int c = 0; c < 2; ++c) CP_HIP(cp::launch_reset(make_args(p, nullptr, nullptr, nullptr, c), p->cap));
+        CP_HIP(hipStreamSynchronize(p->cap));
         int clk_khz = 0;
         if (hipDeviceGetAttribute(&clk_khz, hipDeviceAttributeWallClockRate, p->device) == hipSuccess &&
             clk_khz > 0)
@@ -369,6 +417,79 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
     *out = p;
     return CP_OK;
 }
+
+namespace {
+
+// The layer launches of the sequential and micro-batched modes.  Micro-batched:
+// chunk c of microbatch_rows rows runs its whole chain on side stream c mod 2,
+// forked from and joined back into `s`.
+int enqueue_layers(cp_chain *p, const cp::ChainArgs &a, int32_t mode, int64_t microbatch_rows,
+                   hipStream_t s) {
+    if (mode == CP_MODE_SEQUENTIAL) {
+        const int nrb = (int)(p->M / p->tile_m);
+        for (int l = 0; l < p->L; ++l) CP_HIP(p->var->launch_layer(a, l, 0, nrb, s));
+        return CP_OK;
+    }
+    const int chunk_rb = (int)(microbatch_rows / p->tile_m);
+    const int nchunks = (int)(p->M / microbatch_rows);
+    CP_HIP(hipEventRecord(p->ev_fork, s));
+    for (auto &side : p->side) CP_HIP(hipStreamWaitEvent(side, p->ev_fork, 0));
+    for (int c = 0; c < nchunks; ++c) {
+        hipStream_t cs = p->side[c & 1];
+        for (int l = 0; l < p->L; ++l) CP_HIP(p->var->launch_layer(a, l, c * chunk_rb, chunk_rb, cs));
+    }
+    for (int k = 0; k < 2; ++k) {
+        CP_HIP(hipEventRecord(p->ev_join[k], p->side[k]));
+        CP_HIP(hipStreamWaitEvent(s, p->ev_join[k], 0));
+    }
+    return CP_OK;
+}
+
+// The executable graph of a sequential / micro-batched run on these pointers:
+// captured from the plan's own origin stream on first use, then replayed.
+int find_replay(cp_chain *p, const cp::ChainArgs &a, const void *X, const void *const *W, void *Y,
+                int32_t mode, int64_t mb, hipGraphExec_t *out) {
+    if (mode != CP_MODE_MICROBATCH) mb = 0;
+    for (size_t i = 0; i < p->replays.size(); ++i) {
+        cp_chain::Replay &r = p->replays[i];
+        bool hit = r.mode == mode && r.mb == mb && r.X == X && r.Y == Y;
+        for (int l = 0; hit && l < p->L; ++l) hit = r.W[l] == W[l];
+        if (!hit) continue;
+        std::rotate(p->replays.begin() + i, p->replays.begin() + i + 1, p->replays.end());
+        *out = p->replays.back().exec;
+        return CP_OK;
+    }
+    cp_chain::Replay r;
+    r.mode = mode;
+    r.mb = mb;
+    r.X = X;
+    r.Y = Y;
+    for (int l = 0; l < p->L; ++l) r.W[l] = W[l];
+    CP_HIP(hipStreamBeginCapture(p->cap, hipStreamCaptureModeThreadLocal));
+    int rc = enqueue_layers(p, a, mode, mb, p->cap);
+    hipGraph_t graph = nullptr;
+    const hipError_t e = hipStreamEndCapture(p->cap, &graph);
+    if (rc) {
+        if (graph) (void)hipGraphDestroy(graph);
+        return rc;
+    }
+    CP_HIP(e);
+    r.graph = graph;
+    const hipError_t ei = hipGraphInstantiate(&r.exec, graph, nullptr, nullptr, 0);
+    if (ei != hipSuccess) {
+        drop_replay(r);
+        CP_HIP(ei);
+    }
+    if (p->replays.size() >= kMaxReplays) {
+        drop_replay(p->replays.front());
+        p->replays.erase(p->replays.begin());
+    }
+    p->replays.push_back(r);
+    *out = r.exec;
+    return CP_OK;
+}
+
+}  // namespace
 
 int cp_chain_run(cp_chain *p, const void *X, const void *const *W, void *Y, void *stream,
                  int32_t mode, int64_t microbatch_rows) {
@@ -388,30 +509,35 @@ int cp_chain_run(cp_chain *p, const void *X, const void *const *W, void *Y, void
     CP_HIP(hipGetDevice(&cur));
     if (cur != p->device) return fail(CP_ERR_INVALID_ARG, "current device %d differs from the plan's %d", cur, p->device);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const cp::ChainArgs a = make_args(p, X, W, Y);
+    const cp::ChainArgs a = make_args(p, X, W, Y, p->cur);
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    CP_HIP(hipStreamIsCapturing(s, &cs));
+    if (cs != hipStreamCaptureStatusNone) {
+        // recorded into the caller's graph: kernels only, no timing events
+        if (mode == CP_MODE_PIPELINED)
+            return fail(CP_ERR_UNSUPPORTED, "pipelined mode cannot be captured into a graph (its per-run state alternates between two copies)");
+        if (p->flags & CP_FLAG_POISON)
+            for (int l = 0; l + 1 < p->L; ++l) CP_HIP(cp::launch_poison(p->inter[l], p->inter_bytes[l], p->dtype, s));
+        return enqueue_layers(p, a, mode, microbatch_rows, s);
+    }
 
     CP_HIP(hipEventRecord(p->ev_start, s));
     if (p->flags & CP_FLAG_POISON)
         for (int l = 0; l + 1 < p->L; ++l) CP_HIP(cp::launch_poison(p->inter[l], p->inter_bytes[l], p->dtype, s));
     if (mode == CP_MODE_PIPELINED) {
-        CP_HIP(cp::launch_reset(a, s));
         CP_HIP(hipEventRecord(p->ev_kernel, s));
         CP_HIP(p->var->launch_worker(a, p->n_workers, p->coop, s));
-    } else if (mode == CP_MODE_SEQUENTIAL) {
-        const int nrb = (int)(p->M / p->tile_m);
-        for (int l = 0; l < p->L; ++l) CP_HIP(p->var->launch_layer(a, l, 0, nrb, s));
+        p->last_copy = p->cur;
+        p->cur ^= 1;
     } else {
-        const int chunk_rb = (int)(microbatch_rows / p->tile_m);
-        const int nchunks = (int)(p->M / microbatch_rows);
-        CP_HIP(hipEventRecord(p->ev_fork, s));
-        for (auto &side : p->side) CP_HIP(hipStreamWaitEvent(side, p->ev_fork, 0));
-        for (int c = 0; c < nchunks; ++c) {
-            hipStream_t cs = p->side[c & 1];
-            for (int l = 0; l < p->L; ++l) CP_HIP(p->var->launch_layer(a, l, c * chunk_rb, chunk_rb, cs));
-        }
-        for (int k = 0; k < 2; ++k) {
-            CP_HIP(hipEventRecord(p->ev_join[k], p->side[k]));
-            CP_HIP(hipStreamWaitEvent(s, p->ev_join[k], 0));
+        if (p->flags & CP_FLAG_EAGER) {
+            int rc = enqueue_layers(p, a, mode, microbatch_rows, s);
+            if (rc) return rc;
+        } else {
+            hipGraphExec_t exec = nullptr;
+            int rc = find_replay(p, a, X, W, Y, mode, microbatch_rows, &exec);
+            if (rc) return rc;
+            CP_HIP(hipGraphLaunch(exec, s));
         }
     }
     CP_HIP(hipEventRecord(p->ev_stop, s));
@@ -448,9 +574,10 @@ int cp_chain_stats(cp_chain *p, cp_chain_stats_t *out) {
     uint32_t ctl[cp::kCtlWords];
     std::vector<int32_t> score(T);
     std::vector<uint32_t> queue(T);
-    CP_HIP(hipMemcpy(ctl, p->d_ctl, sizeof ctl, hipMemcpyDeviceToHost));
-    CP_HIP(hipMemcpy(score.data(), p->d_score, T * 4, hipMemcpyDeviceToHost));
-    CP_HIP(hipMemcpy(queue.data(), p->d_queue, T * 4, hipMemcpyDeviceToHost));
+    const int c = p->last_copy;
+    CP_HIP(hipMemcpy(ctl, p->d_ctl[c], sizeof ctl, hipMemcpyDeviceToHost));
+    CP_HIP(hipMemcpy(score.data(), p->d_score[c], T * 4, hipMemcpyDeviceToHost));
+    CP_HIP(hipMemcpy(queue.data(), p->d_queue[c], T * 4, hipMemcpyDeviceToHost));
     out->status = (int32_t)ctl[cp::kCtlStatus];
     out->n_queues = p->nq;
     out->queues_drained = 1;
@@ -475,14 +602,14 @@ int cp_chain_stats(cp_chain *p, cp_chain_stats_t *out) {
     out->queue_is_perm = perm ? 1 : 0;
     if (p->flags & CP_FLAG_DEBUG) {
         std::vector<uint32_t> deq(T);
-        CP_HIP(hipMemcpy(deq.data(), p->d_deq, T * 4, hipMemcpyDeviceToHost));
+        CP_HIP(hipMemcpy(deq.data(), p->d_deq[c], T * 4, hipMemcpyDeviceToHost));
         int32_t bad = 0;
         for (size_t t = 0; t < T; ++t) bad += deq[t] != 1;
         out->bad_dequeues = bad;
     }
     if (p->flags & CP_FLAG_TRACE) {
         std::vector<uint64_t> tr(T * 4);
-        CP_HIP(hipMemcpy(tr.data(), p->d_trace, T * 32, hipMemcpyDeviceToHost));
+        CP_HIP(hipMemcpy(tr.data(), p->d_trace[c], T * 32, hipMemcpyDeviceToHost));
         int32_t viol = 0;
         for (size_t pr = 0; pr < T; ++pr)
             for (int32_t e = p->g.dep_off[pr]; e < p->g.dep_off[pr + 1]; ++e) {
@@ -501,7 +628,7 @@ int cp_chain_trace(cp_chain *p, uint64_t *out, int64_t capacity) {
     if (!(p->flags & CP_FLAG_TRACE)) return fail(CP_ERR_INVALID_ARG, "plan was built without CP_FLAG_TRACE");
     if (capacity < 4 * (int64_t)p->g.T) return fail(CP_ERR_INVALID_ARG, "capacity %lld < 4*T", (long long)capacity);
     if (p->ran) CP_HIP(hipEventSynchronize(p->ev_stop));
-    CP_HIP(hipMemcpy(out, p->d_trace, (size_t)p->g.T * 32, hipMemcpyDeviceToHost));
+    CP_HIP(hipMemcpy(out, p->d_trace[p->last_copy], (size_t)p->g.T * 32, hipMemcpyDeviceToHost));
     return CP_OK;
 }
 

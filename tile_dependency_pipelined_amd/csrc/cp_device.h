@@ -58,6 +58,12 @@ struct ChainArgs {
     const uint32_t *qinit;   // [T] initial queue contents (reset source)
     uint32_t *deq_count;     // [T] debug: dequeues per tile, or null
     uint64_t *trace;         // [4T] timestamps, or null
+    // the other copy of the per-run state (queue, ctl, score, deq_count,
+    // trace), used by the next pipelined run; this run's workers reset it
+    uint32_t *nxt_queue, *nxt_ctl;
+    int32_t *nxt_score;
+    uint32_t *nxt_deq_count;
+    uint64_t *nxt_trace;
     uint64_t timeout_ticks;  // watchdog on a queue wait, 100 MHz ticks
 };
 

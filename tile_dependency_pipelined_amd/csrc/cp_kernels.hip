@@ -467,8 +467,9 @@ __device__ __forceinline__ uint32_t ld_relaxed(const uint32_t *p) {
 // below it is claimed and filled without waiting.  Take an unfinished tile
 // of lowest layer: its producers are finished, so it has been pushed, and
 // the workers of its queue reach it.  Every queue has workers and all
-// workers are co-resident (cooperative launch), so no wait lasts forever
-// for a well-formed dependency table.
+// workers are resident (the grid fits the device at once), so no wait lasts
+// forever for a well-formed dependency table; if the device is shared and
+// some workers are not resident, the watchdog ends the run with a timeout.
 __device__ uint32_t prologue(const ChainArgs &a, int q) {
     if (ld_relaxed(a.ctl + kCtlStatus) != 0) return kDone;
     const uint32_t t = __hip_atomic_fetch_add(a.ctl + ctl_head(q), 1u, __ATOMIC_RELAXED,
@@ -565,18 +566,48 @@ __device__ __forceinline__ void decode(const ChainArgs &a, uint32_t id, int &l, 
 // Kernels
 // ----------------------------------------------------------------------------
 
+// Per-run state reset of one copy: scoreboard from the in-degree template,
+// queues from their initial image (each pre-filled with its first-layer
+// tiles in row-block-major order, EMPTY after), per-queue head = 0,
+// tail = pre-filled, status OK.  Grid-stride over the calling grid.
+__device__ void reset_copy(const ChainArgs &a, uint32_t *queue, uint32_t *ctl, int32_t *score,
+                           uint32_t *deq_count, uint64_t *trace) {
+    const int stride = gridDim.x * blockDim.x;
+    for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < a.T; t += stride) {
+        score[t] = a.indeg[t];
+        queue[t] = a.qinit[t];
+        if (deq_count) deq_count[t] = 0;
+        if (trace) {
+            trace[4 * (size_t)t + 0] = 0;
+            trace[4 * (size_t)t + 1] = 0;
+            trace[4 * (size_t)t + 2] = 0;
+            trace[4 * (size_t)t + 3] = 0;
+        }
+    }
+    if (blockIdx.x == 0 && threadIdx.x < kMaxQueues) {
+        const int q = threadIdx.x;
+        ctl[ctl_head(q)] = 0;
+        ctl[ctl_tail(q)] = q < a.nq ? (uint32_t)a.qfirst[q] : 0u;
+        if (q == 0) ctl[kCtlStatus] = 0;
+    }
+}
+
 // Persistent worker: loop prologue -> tile body -> publish until its queue
 // (blockIdx.x mod nq, so that workgroups dispatched round-robin over the
-// XCDs serve the queue of their own XCD) is exhausted.  Launched
-// cooperatively: all workers are co-resident.  The tile ID is broadcast
-// through the first word of stage 0; the second barrier guarantees every
-// thread has read it before the body's loads reuse stage 0.
+// XCDs serve the queue of their own XCD) is exhausted.  The grid is the
+// number of workgroups the device holds at once, so on an otherwise idle
+// device every worker is resident (a cooperative launch guarantees it).
+// First, the workers reset the other copy of the per-run state for the next
+// run (nothing of this run reads it; the kernel boundary publishes it).  The
+// tile ID is broadcast through the first word of stage 0; the second barrier
+// guarantees every thread has read it before the body's loads reuse stage 0.
 template <class Body>
 __global__ void __launch_bounds__(Body::NT) worker_kernel(ChainArgs a) {
     char *stg[5];
     Stages<Body>::get(stg);
     volatile uint32_t *slot = reinterpret_cast<volatile uint32_t *>(stg[0]);
     const int q = (int)(blockIdx.x % (unsigned)a.nq);
+    reset_copy(a, a.nxt_queue, a.nxt_ctl, a.nxt_score, a.nxt_deq_count, a.nxt_trace);
     for (;;) {
         if (threadIdx.x == 0) *slot = prologue(a, q);
         __syncthreads();
@@ -604,29 +635,8 @@ __global__ void __launch_bounds__(Body::NT) layer_kernel(ChainArgs a, int l, int
     Body::run(d, i, j, stg);
 }
 
-// Per-run state reset: scoreboard from the in-degree template, queues from
-// their initial image (each pre-filled with its first-layer tiles in
-// row-block-major order, EMPTY after), per-queue head = 0, tail = pre-filled.
-__global__ void reset_kernel(ChainArgs a) {
-    const int stride = gridDim.x * blockDim.x;
-    for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < a.T; t += stride) {
-        a.score[t] = a.indeg[t];
-        a.queue[t] = a.qinit[t];
-        if (a.deq_count) a.deq_count[t] = 0;
-        if (a.trace) {
-            a.trace[4 * (size_t)t + 0] = 0;
-            a.trace[4 * (size_t)t + 1] = 0;
-            a.trace[4 * (size_t)t + 2] = 0;
-            a.trace[4 * (size_t)t + 3] = 0;
-        }
-    }
-    if (blockIdx.x == 0 && threadIdx.x < kMaxQueues) {
-        const int q = threadIdx.x;
-        a.ctl[ctl_head(q)] = 0;
-        a.ctl[ctl_tail(q)] = q < a.nq ? (uint32_t)a.qfirst[q] : 0u;
-        if (q == 0) a.ctl[kCtlStatus] = 0;
-    }
-}
+// Reset of the current copy (at plan time, for both copies).
+__global__ void reset_kernel(ChainArgs a) { reset_copy(a, a.queue, a.ctl, a.score, a.deq_count, a.trace); }
 
 // Fill an intermediate with quiet NaN so that a premature read is visible.
 __global__ void poison_kernel(uint32_t *p, size_t words, uint32_t pattern) {
