@@ -37,8 +37,8 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="c3")
     ap.add_argument("--tile", default=None, help="override tile, e.g. 256x128")
     ap.add_argument("--reps", type=int, default=20, help="reps per mode for the baseline comparison")
@@ -88,8 +88,8 @@ def main():
     plan = ch.Chain(cfg.M, cfg.widths, cfg.dtype, tile[0], tile[1], acts=list(cfg.acts))
     stream = torch.cuda.current_stream()
 
-    def step(mode="pipelined", mb=0):
-        plan.run(dX, dW, dY, mode=mode, microbatch_rows=mb, stream=stream)
+    def step(mode="pipelined", mb=0, p=plan):
+        p.run(dX, dW, dY, mode=mode, microbatch_rows=mb, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -97,7 +97,10 @@ def main():
     st = plan.stats()
     assert st["status"] == 0 and st["nonzero_scores"] == 0 and st["queue_is_perm"] == 1, st
 
-    # ---- timed region: exactly K steps between two synchronisations
+    # ---- timed region: exactly K steps between two synchronisations.  A
+    # pipelined step is one launch of the persistent worker kernel on
+    # `stream`, so the HIP events on that stream also time the kernel:
+    # per-launch duration = elapsed / K (back-to-back launches).
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -111,16 +114,18 @@ def main():
     wall_ms = (w1 - w0) * 1e3 / args.steps
     ev_ms = ev0.elapsed_time(ev1) / args.steps
     log(f"timed: {args.steps} steps, {wall_ms * 1e3:.1f} us/step wall, {ev_ms * 1e3:.1f} us/step events")
+    kernel_ms = ev_ms
 
-    # worker kernel alone (HIP events on the launch stream, inside the library)
-    kern, runs = [], []
-    for _ in range(args.steps):
-        step()
-        s = plan.stats()
-        kern.append(s["last_kernel_ms"])
-        runs.append(s["last_run_ms"])
-    kernel_ms = statistics.mean(kern)
-    log(f"worker kernel {kernel_ms * 1e3:.1f} us mean, run {statistics.mean(runs) * 1e3:.1f} us mean")
+    # one isolated launch at a time, bracketed by the library's own events
+    # (CP_FLAG_TIMING) -- includes the events' own stream stalls
+    iso = []
+    with ch.Chain(cfg.M, cfg.widths, cfg.dtype, tile[0], tile[1], acts=list(cfg.acts),
+                  flags=nat.CP_FLAG_TIMING) as pt:
+        for _ in range(min(args.steps, 50)):
+            step(p=pt)
+            iso.append(pt.stats()["last_kernel_ms"])
+    iso_ms = statistics.median(iso)
+    log(f"isolated launch {iso_ms * 1e3:.1f} us median")
 
     peak = PEAK_BF16_TFLOPS if cfg.dtype == gen.BF16 else PEAK_FP32_TFLOPS
     flops = cfg.flops
@@ -167,6 +172,7 @@ def main():
         "traffic": traffic,
         "kernel": "cp::worker_kernel<Bf16Body<%d,%d,...>>" % tile if cfg.dtype == gen.BF16 else "worker_kernel<F32Body>",
         "kernel_us": round(kernel_ms * 1e3, 1),
+        "kernel_us_isolated_median": round(iso_ms * 1e3, 1),
         "algorithmic_flop_per_launch": flops,
         "algorithmic_bytes_min": cfg.min_bytes(),
         "hbm_frac_min_bytes": round(cfg.min_bytes() / (kernel_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),

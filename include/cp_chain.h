@@ -85,6 +85,17 @@ typedef struct cp_chain cp_chain; /* opaque plan */
  * relies on the device being otherwise idle (else the watchdog may end the
  * run with CP_ERR_TIMEOUT) */
 #define CP_FLAG_COOPERATIVE 64u
+/* pipelined mode: release every producer tile with an agent-scope fence
+ * (write-back of its XCD's whole L2) and acquire every consumer tile with an
+ * L2 invalidate, the plain memory-model protocol.  Default: intermediates are
+ * stored at agent scope (write-through), each producer waits until its stores
+ * have completed before it decrements a counter, and consumers need no
+ * invalidate */
+#define CP_FLAG_FENCE_RELEASE 128u
+/* record HIP timing events around every run (cp_chain_stats then reports
+ * last_run_ms / last_kernel_ms); each event stalls the stream for a few
+ * microseconds, so untimed plans record only one completion event */
+#define CP_FLAG_TIMING 256u
 
 #define CP_MAX_LAYERS 8
 
@@ -105,9 +116,10 @@ typedef struct cp_chain_stats_t {
     int32_t n_queues;        /* work-queues (one per XCD)                                 */
     int32_t queues_drained;  /* 1 if every queue was filled to its size and fully taken   */
     int32_t order_violations;/* TRACE only: consumers that started before a producer ended */
-    double last_run_ms;      /* elapsed time of the last run, from events on its stream   */
-    double last_kernel_ms;   /* pipelined: the persistent launch alone (reset excluded);
-                                other modes: same as last_run_ms                          */
+    double last_run_ms;      /* elapsed time of the last run, from events on its stream
+                                (plans built with CP_FLAG_TIMING; -1 otherwise)           */
+    double last_kernel_ms;   /* pipelined with CP_FLAG_POISON: the persistent launch alone
+                                (poison fills excluded); otherwise same as last_run_ms    */
 } cp_chain_stats_t;
 
 /*
@@ -162,7 +174,9 @@ int cp_chain_run(cp_chain *plan, const void *X, const void *const *W, void *Y,
 /*
  * cp_chain_stats -- synchronise with the plan's last run and report status,
  * timing and the scoreboard/queue invariants (every
- * counter ends at 0, every tile dequeued exactly once).
+ * counter ends at 0, every tile dequeued exactly once).  Without
+ * CP_FLAG_TIMING it synchronises the last run's stream, which must still
+ * exist; cp_chain_trace likewise.
  */
 int cp_chain_stats(cp_chain *plan, cp_chain_stats_t *out);
 
@@ -175,7 +189,8 @@ int cp_chain_stats(cp_chain *plan, cp_chain_stats_t *out);
  */
 int cp_chain_trace(cp_chain *plan, uint64_t *out, int64_t capacity);
 
-/* cp_chain_destroy -- wait for the plan's work and free it.  NULL is a no-op. */
+/* cp_chain_destroy -- wait for the device (the plan's last stream may be
+ * gone) and free the plan.  NULL is a no-op. */
 int cp_chain_destroy(cp_chain *plan);
 
 /*

@@ -133,20 +133,23 @@ def test_bf16_small_parity(rt, tile):
     assert same_bits(out["pipelined"], out["microbatch"])
 
 
+@pytest.mark.parametrize("release", ["write-through", "fence"])
 @pytest.mark.parametrize("dtype", [gen.F32, gen.BF16], ids=["f32", "bf16"])
-def test_signed_permutation_chain_exact_with_poison(rt, dtype):
+def test_signed_permutation_chain_exact_with_poison(rt, dtype, release):
     """X . P1 D1 . P2 D2 . P3 D3 is exact in every element type, so the GPU
     result must equal the oracle bit for bit; intermediates are NaN-poisoned
     before every run and a quarter of producers are delayed, so a consumer
-    that read an intermediate before its producers published would show."""
+    that read an intermediate before its producers published would show.
+    Both release protocols (write-through stores, or a fence per tile)."""
     f = rt_flags()
+    extra = rt["nat"].CP_FLAG_FENCE_RELEASE if release == "fence" else 0
     tile = (64, 64) if dtype == gen.F32 else (128, 128)
     n = 512 if dtype == gen.F32 else 1024
     M = 4 * tile[0]
     X = gen.normal_matrix((M, n), 1.0, 60, dtype)
     Ws = [gen.signed_permutation(n, 61 + l, dtype, scale_pow2=s) for l, s in enumerate((1, -2, 0))]
-    say("perm chain", dtype, tile, M, n)
-    out, st = run_modes(rt, X, Ws, dtype, tile, flags=all_flags() | f["DELAY"],
+    say("perm chain", dtype, tile, M, n, release)
+    out, st = run_modes(rt, X, Ws, dtype, tile, flags=all_flags() | f["DELAY"] | extra,
                         modes=("pipelined", "sequential"), reps=3)
     ref = oracle.chain(X, Ws, dtype)
     assert np.array_equal(as_values(out["pipelined"], dtype), ref)

@@ -149,7 +149,9 @@ struct cp_chain {
         hipGraphExec_t exec = nullptr;
     };
     std::vector<Replay> replays;       // most recently used last
-    hipEvent_t ev_start = nullptr, ev_kernel = nullptr, ev_stop = nullptr;
+    hipEvent_t ev_start = nullptr, ev_kernel = nullptr, ev_stop = nullptr;  // CP_FLAG_TIMING
+    hipStream_t last_stream = nullptr; // stream of the last run
+    bool timed = false;                // the last run recorded timing events
     uint64_t timeout_ticks = 200000000ull;  // 2 s at 100 MHz
     int32_t last_mode = -1;
     bool ran = false;
@@ -186,7 +188,8 @@ void release(cp_chain *p) {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-cp::ChainArgs make_args(const cp_chain *p, const void *X, const void *const *W, void *Y, int copy) {
+cp::ChainArgs make_args(const cp_chain *p, const void *X, const void *const *W, void *Y, int copy,
+                        int32_t mode = CP_MODE_PIPELINED) {
     cp::ChainArgs a;
     memset(&a, 0, sizeof a);
     const size_t es = p->dtype == CP_BF16 ? 2 : 4;
@@ -200,6 +203,7 @@ cp::ChainArgs make_args(const cp_chain *p, const void *X, const void *const *W, 
         d.N = (int32_t)p->widths[l + 1];
         d.nbn = p->g.nbn[l];
         d.act = p->acts[l];
+        d.coherent = (mode == CP_MODE_PIPELINED && l + 1 < p->L && !(p->flags & CP_FLAG_FENCE_RELEASE)) ? 1 : 0;
         d.tile_off = p->g.layer_off[l];
         d.ntiles = p->g.layer_off[l + 1] - p->g.layer_off[l];
     }
@@ -291,7 +295,7 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
             if (acts[l] != CP_ACT_NONE && acts[l] != CP_ACT_GELU_TANH)
                 return fail(CP_ERR_INVALID_ARG, "acts[%d] = %d", l, acts[l]);
     const uint32_t known = CP_FLAG_DEBUG | CP_FLAG_TRACE | CP_FLAG_POISON | CP_FLAG_DELAY_INJECT | CP_FLAG_STARVE_LAST |
-                           CP_FLAG_EAGER | CP_FLAG_COOPERATIVE;
+                           CP_FLAG_EAGER | CP_FLAG_COOPERATIVE | CP_FLAG_FENCE_RELEASE | CP_FLAG_TIMING;
     if (flags & ~known) return fail(CP_ERR_INVALID_ARG, "unknown flags 0x%x", flags & ~known);
     if ((flags & CP_FLAG_STARVE_LAST) && n_layers < 2)
         return fail(CP_ERR_INVALID_ARG, "CP_FLAG_STARVE_LAST needs at least two layers");
@@ -509,7 +513,7 @@ int cp_chain_run(cp_chain *p, const void *X, const void *const *W, void *Y, void
     CP_HIP(hipGetDevice(&cur));
     if (cur != p->device) return fail(CP_ERR_INVALID_ARG, "current device %d differs from the plan's %d", cur, p->device);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const cp::ChainArgs a = make_args(p, X, W, Y, p->cur);
+    const cp::ChainArgs a = make_args(p, X, W, Y, p->cur, mode);
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     CP_HIP(hipStreamIsCapturing(s, &cs));
     if (cs != hipStreamCaptureStatusNone) {
@@ -521,11 +525,14 @@ int cp_chain_run(cp_chain *p, const void *X, const void *const *W, void *Y, void
         return enqueue_layers(p, a, mode, microbatch_rows, s);
     }
 
-    CP_HIP(hipEventRecord(p->ev_start, s));
+    // Timing events stall the stream for a few microseconds each, so they
+    // are recorded only when the plan asks for them.
+    const bool timed = (p->flags & CP_FLAG_TIMING) != 0;
+    if (timed) CP_HIP(hipEventRecord(p->ev_start, s));
     if (p->flags & CP_FLAG_POISON)
         for (int l = 0; l + 1 < p->L; ++l) CP_HIP(cp::launch_poison(p->inter[l], p->inter_bytes[l], p->dtype, s));
     if (mode == CP_MODE_PIPELINED) {
-        CP_HIP(hipEventRecord(p->ev_kernel, s));
+        if (timed && (p->flags & CP_FLAG_POISON)) CP_HIP(hipEventRecord(p->ev_kernel, s));
         CP_HIP(p->var->launch_worker(a, p->n_workers, p->coop, s));
         p->last_copy = p->cur;
         p->cur ^= 1;
@@ -540,11 +547,25 @@ int cp_chain_run(cp_chain *p, const void *X, const void *const *W, void *Y, void
             CP_HIP(hipGraphLaunch(exec, s));
         }
     }
-    CP_HIP(hipEventRecord(p->ev_stop, s));
+    if (timed) CP_HIP(hipEventRecord(p->ev_stop, s));
+    p->timed = timed;
+    p->last_stream = s;
     p->last_mode = mode;
     p->ran = true;
     return CP_OK;
 }
+
+namespace {
+
+// Wait for the plan's last run: its stop event when timed, else its stream.
+int wait_last(cp_chain *p) {
+    if (!p->ran) return CP_OK;
+    if (p->timed) CP_HIP(hipEventSynchronize(p->ev_stop));
+    else CP_HIP(hipStreamSynchronize(p->last_stream));
+    return CP_OK;
+}
+
+}  // namespace
 
 int cp_chain_stats(cp_chain *p, cp_chain_stats_t *out) {
     g_last_error.clear();
@@ -560,15 +581,22 @@ int cp_chain_stats(cp_chain *p, cp_chain_stats_t *out) {
     out->tile_n = p->tile_n;
     out->bad_dequeues = -1;
     out->order_violations = -1;
+    out->last_run_ms = -1.0;
+    out->last_kernel_ms = -1.0;
     if (!p->ran) return CP_OK;
-    CP_HIP(hipEventSynchronize(p->ev_stop));
-    float ms = 0.f;
-    CP_HIP(hipEventElapsedTime(&ms, p->ev_start, p->ev_stop));
-    out->last_run_ms = ms;
-    out->last_kernel_ms = ms;
+    int rc = wait_last(p);
+    if (rc) return rc;
+    if (p->timed) {
+        float ms = 0.f;
+        CP_HIP(hipEventElapsedTime(&ms, p->ev_start, p->ev_stop));
+        out->last_run_ms = ms;
+        out->last_kernel_ms = ms;
+        if (p->last_mode == CP_MODE_PIPELINED && (p->flags & CP_FLAG_POISON)) {
+            CP_HIP(hipEventElapsedTime(&ms, p->ev_kernel, p->ev_stop));
+            out->last_kernel_ms = ms;
+        }
+    }
     if (p->last_mode != CP_MODE_PIPELINED) return CP_OK;
-    CP_HIP(hipEventElapsedTime(&ms, p->ev_kernel, p->ev_stop));
-    out->last_kernel_ms = ms;
 
     const size_t T = (size_t)p->g.T;
     uint32_t ctl[cp::kCtlWords];
@@ -627,7 +655,8 @@ int cp_chain_trace(cp_chain *p, uint64_t *out, int64_t capacity) {
     if (!p || !out) return fail(CP_ERR_INVALID_ARG, "plan or out is NULL");
     if (!(p->flags & CP_FLAG_TRACE)) return fail(CP_ERR_INVALID_ARG, "plan was built without CP_FLAG_TRACE");
     if (capacity < 4 * (int64_t)p->g.T) return fail(CP_ERR_INVALID_ARG, "capacity %lld < 4*T", (long long)capacity);
-    if (p->ran) CP_HIP(hipEventSynchronize(p->ev_stop));
+    int rc = wait_last(p);
+    if (rc) return rc;
     CP_HIP(hipMemcpy(out, p->d_trace[p->last_copy], (size_t)p->g.T * 32, hipMemcpyDeviceToHost));
     return CP_OK;
 }
@@ -635,7 +664,7 @@ int cp_chain_trace(cp_chain *p, uint64_t *out, int64_t capacity) {
 int cp_chain_destroy(cp_chain *p) {
     g_last_error.clear();
     if (!p) return CP_OK;
-    if (p->ran) (void)hipEventSynchronize(p->ev_stop);
+    if (p->ran) (void)hipDeviceSynchronize();  // the last run's stream may be gone
     for (auto &s : p->side)
         if (s) (void)hipStreamSynchronize(s);
     release(p);

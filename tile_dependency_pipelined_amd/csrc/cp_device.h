@@ -37,6 +37,7 @@ struct LayerDesc {
     int32_t act;       // CP_ACT_*
     int32_t tile_off;  // flat ID of this layer's first tile
     int32_t ntiles;    // (M / tile_m) * nbn
+    int32_t coherent;  // store C at agent scope (write-through of the XCD's L2)
 };
 
 // Everything one launch needs, passed by value as the kernel argument.

@@ -302,24 +302,71 @@ struct Bf16Body {
         wait_vmcnt<0>();  // the trailing prefetches must land before the LDS is reused
         __syncthreads();
 
-        // epilogue: activation on the fp32 accumulator, RNE to bf16, 8-byte stores
+        // Epilogue: activation on the fp32 accumulator, RNE to bf16, then the
+        // tile goes through the (now idle) LDS stages so that every store
+        // instruction writes whole contiguous rows (64 lanes x 8 bytes):
+        // full 128-byte lines, which write-through stores need to run at
+        // full speed.  LDS layout: row r in stage r / RPS, 16-byte chunk c
+        // at position c ^ (r mod CPR), which spreads the 32 rows written by
+        // one fragment store over distinct bank groups.
+        constexpr int CPR = BN / 8;                // 16-byte chunks per row
+        constexpr int RPS0 = STAGE / (BN * 2);     // tile rows one stage holds
+        constexpr int RPS = RPS0 >= BM ? BM : RPS0;  // tile rows per stage used
+        constexpr int UPR = BN / 4;                // 8-byte units per row
+        static_assert(RPS % 32 == 0 && RPS * S >= BM && NT % UPR == 0 && RPS % (NT / UPR) == 0,
+                      "epilogue staging");
+        auto stage_of = [&](int k) -> char * {     // k uniform; no dynamic array indexing
+            char *p = stg[0];
+            if constexpr (S > 1) p = k == 1 ? stg[1] : p;
+            if constexpr (S > 2) p = k == 2 ? stg[2] : p;
+            if constexpr (S > 3) p = k == 3 ? stg[3] : p;
+            if constexpr (S > 4) p = k == 4 ? stg[4] : p;
+            return p;
+        };
         const int act = d.act;
+        const int h8 = (lane >> 5) * 8;            // byte half of a 16-byte chunk
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
-            const int m = row0 + wm * WM + fm * 32 + (lane & 31);
-            uint16_t *crow = C + (size_t)m * N + col0 + wn * WN;
+            const int rb = wm * WM + fm * 32;      // first row of this fragment block (uniform)
+            const int r = rb + (lane & 31);
+            char *rowp = stage_of(rb / RPS) + (r % RPS) * (BN * 2) + h8;
+            const int key = r % CPR;
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn)
+            for (int fn = 0; fn < FN; ++fn) {
+                const int c0 = (wn * WN + fn * 32) / 8;
+                const f32x16_t &v = acc[fm][fn];
 #pragma unroll
                 for (int gq = 0; gq < 4; ++gq) {
-                    const int n = fn * 32 + gq * 8 + (lane >> 5) * 4;
-                    const f32x16_t &v = acc[fm][fn];
                     const uint32_t b0 = f32_to_bf16_rne(act_apply(v[4 * gq + 0], act));
                     const uint32_t b1 = f32_to_bf16_rne(act_apply(v[4 * gq + 1], act));
                     const uint32_t b2 = f32_to_bf16_rne(act_apply(v[4 * gq + 2], act));
                     const uint32_t b3 = f32_to_bf16_rne(act_apply(v[4 * gq + 3], act));
-                    *reinterpret_cast<uint2 *>(crow + n) = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+                    *reinterpret_cast<uint2 *>(rowp + (((c0 + gq) ^ key) << 4)) =
+                        make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
                 }
+            }
+        }
+        __syncthreads();
+        // An intermediate consumed by other XCDs while the run goes on is
+        // stored at agent scope, which writes through this XCD's L2.
+        constexpr int RPI = NT / UPR;              // rows per store instruction
+        constexpr int NI = BM / RPI;               // store instructions per lane
+        const int t = tid / UPR, u = tid % UPR;
+        const int lds_u = (u & 1) * 8;
+        uint64_t *dst = reinterpret_cast<uint64_t *>(C + (size_t)(row0 + t) * N + col0 + u * 4);
+        auto lds_at = [&](int it) {
+            const int r = it * RPI + t;
+            return reinterpret_cast<const uint64_t *>(stage_of((it * RPI) / RPS) + (r % RPS) * (BN * 2) +
+                                                      (((u >> 1) ^ (r % CPR)) << 4) + lds_u);
+        };
+        if (__builtin_amdgcn_readfirstlane(d.coherent)) {
+#pragma unroll
+            for (int it = 0; it < NI; ++it)
+                __hip_atomic_store(dst + (size_t)it * RPI * N / 4, *lds_at(it), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+#pragma unroll
+            for (int it = 0; it < NI; ++it) dst[(size_t)it * RPI * N / 4] = *lds_at(it);
         }
     }
 };
@@ -401,9 +448,18 @@ struct F32Body {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int n = g * 8 + (lane >> 5) * 4;
-            *reinterpret_cast<float4 *>(crow + n) =
-                make_float4(act_apply(acc[4 * g + 0], act), act_apply(acc[4 * g + 1], act),
-                            act_apply(acc[4 * g + 2], act), act_apply(acc[4 * g + 3], act));
+            const float4 v = make_float4(act_apply(acc[4 * g + 0], act), act_apply(acc[4 * g + 1], act),
+                                         act_apply(acc[4 * g + 2], act), act_apply(acc[4 * g + 3], act));
+            if (d.coherent) {  // agent scope: writes through this XCD's L2
+                const uint64_t lo = (uint64_t)__float_as_uint(v.x) | ((uint64_t)__float_as_uint(v.y) << 32);
+                const uint64_t hi = (uint64_t)__float_as_uint(v.z) | ((uint64_t)__float_as_uint(v.w) << 32);
+                __hip_atomic_store(reinterpret_cast<uint64_t *>(crow + n), lo, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(reinterpret_cast<uint64_t *>(crow + n + 2), hi, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+                *reinterpret_cast<float4 *>(crow + n) = v;
+            }
         }
     }
 };
@@ -490,10 +546,15 @@ __device__ uint32_t prologue(const ChainArgs &a, int q) {
             if (ld_relaxed(a.ctl + kCtlStatus) != 0) return kDone;
         }
     }
-    if (id >= (uint32_t)a.layer[0].ntiles) {
+    if (id >= (uint32_t)a.layer[0].ntiles && (a.flags & CP_FLAG_FENCE_RELEASE)) {
         // Every producer of `id` released its stores before decrementing
         // score[id]; acquiring the final value (0) of that counter orders this
-        // workgroup's subsequent loads after all of those stores.
+        // workgroup's subsequent loads after all of those stores (and
+        // invalidates this XCD's L2).  With write-through release (default)
+        // no invalidate is needed: the run's reads of an intermediate
+        // row-block all come after its producers finished, the caches held
+        // none of its lines at kernel start, and the producers' agent-scope
+        // stores reached memory before any counter was decremented.
         (void)__hip_atomic_load(a.score + id, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (a.deq_count)
@@ -505,17 +566,25 @@ __device__ uint32_t prologue(const ChainArgs &a, int q) {
     return id;
 }
 
-// All threads.  Called after the tile's stores.  The barrier makes every
-// wave's stores happen-before wave 0's agent-scope release (write-back of
-// this XCD's L2); wave 0 then decrements the counter of every consumer (all
-// in layer l+1), one edge per lane, and pushes the consumers whose counter
-// reached zero into their owner queues, one tail atomic per queue.
+// All threads.  Called after the tile's stores.  Release, two ways:
+//   write-through (default): the tile was stored at agent scope, which
+//     writes through this XCD's L2; every wave waits until its stores have
+//     completed (vmcnt 0) before the barrier, so all of them are in memory
+//     before wave 0 touches a counter.  No L2 write-back is needed.
+//   CP_FLAG_FENCE_RELEASE: the barrier makes every wave's (write-back)
+//     stores happen-before wave 0's agent-scope release fence, which writes
+//     back this XCD's whole L2.
+// Wave 0 then decrements the counter of every consumer (all in layer l+1),
+// one edge per lane, and pushes the consumers whose counter reached zero into
+// their owner queues, one tail atomic per queue.
 __device__ void publish(const ChainArgs &a, uint32_t id, int l) {
+    const bool fenced = (a.flags & CP_FLAG_FENCE_RELEASE) != 0;
+    if (!fenced) wait_vmcnt<0>();
     __syncthreads();
     const int tid = threadIdx.x;
     if (tid >= 64) return;
     const int lane = tid;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (fenced) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     if ((a.flags & CP_FLAG_DELAY_INJECT) && ((id * 2654435761u) >> 30) == 0) {
         const uint64_t s = wall_clock64();
         while (wall_clock64() - s < 2000) __builtin_amdgcn_s_sleep(8);  // ~20 us

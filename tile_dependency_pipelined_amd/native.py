@@ -29,6 +29,8 @@ CP_FLAG_DELAY_INJECT = 8
 CP_FLAG_STARVE_LAST = 16
 CP_FLAG_EAGER = 32
 CP_FLAG_COOPERATIVE = 64
+CP_FLAG_FENCE_RELEASE = 128
+CP_FLAG_TIMING = 256
 CP_MAX_LAYERS = 8
 
 # every symbol include/cp_chain.h declares
