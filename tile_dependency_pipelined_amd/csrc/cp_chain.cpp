@@ -211,6 +211,7 @@ cp::ChainArgs make_args(const cp_chain *p, const void *X, const void *const *W, 
     a.T = p->g.T;
     a.flags = p->flags;
     a.nq = p->nq;
+    a.nworkers = p->n_workers;
     for (int q = 0; q < cp::kMaxQueues; ++q) {
         a.qbase[q] = p->qbase[q];
         a.qsize[q] = p->qsize[q];

@@ -130,7 +130,11 @@ struct Bf16Body {
         else return (k & 3) << 1;
     }
 
-    __device__ __forceinline__ static void run(const LayerDesc &d, int i, int j, char *const *stg) {
+    // `before_epilogue` runs in every thread once the main loop is done (the
+    // worker takes its next ticket there).
+    template <class Hook>
+    __device__ __forceinline__ static void run(const LayerDesc &d, int i, int j, char *const *stg,
+                                               Hook &&before_epilogue) {
         const uint16_t *__restrict__ A = static_cast<const uint16_t *>(d.A);
         const uint16_t *__restrict__ W = static_cast<const uint16_t *>(d.W);
         uint16_t *__restrict__ C = static_cast<uint16_t *>(d.C);
@@ -301,6 +305,7 @@ struct Bf16Body {
         if constexpr (S > 4) if (slab < nk) step(ic<3 % S>{}, slab++);
         wait_vmcnt<0>();  // the trailing prefetches must land before the LDS is reused
         __syncthreads();
+        before_epilogue();
 
         // Epilogue: activation on the fp32 accumulator, RNE to bf16, then the
         // tile goes through the (now idle) LDS stages so that every store
@@ -382,7 +387,11 @@ struct F32Body {
     static constexpr int BP = BN + 4;  // padded W row ([k][n]), keeps 16-byte alignment
     static constexpr int STAGE = (BK * AP + BK * BP) * 4;
 
-    __device__ __forceinline__ static void run(const LayerDesc &d, int i, int j, char *const *stg) {
+    // `before_epilogue` runs in every thread once the main loop is done (the
+    // worker takes its next ticket there).
+    template <class Hook>
+    __device__ __forceinline__ static void run(const LayerDesc &d, int i, int j, char *const *stg,
+                                               Hook &&before_epilogue) {
         const float *__restrict__ A = static_cast<const float *>(d.A);
         const float *__restrict__ W = static_cast<const float *>(d.W);
         float *__restrict__ C = static_cast<float *>(d.C);
@@ -441,6 +450,7 @@ struct F32Body {
             if (ks + 1 < nk) lstore(stg[(ks + 1) & 1]);
             __syncthreads();
         }
+        before_epilogue();
 
         const int act = d.act;
         const int m = row0 + wm * 32 + (lane & 31);
@@ -513,23 +523,30 @@ __device__ __forceinline__ uint32_t ld_relaxed(const uint32_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Thread 0 only.  Take the next slot (ticket) of this worker's queue q, wait
-// until a tile ID has been pushed into it, and make the producers' stores of
-// that tile's inputs visible.  Returns the tile ID, or kDone when the queue
-// is exhausted or the run has failed.
+// Scheduler lane only.  take_ticket claims the next slot (ticket) of this
+// worker's queue q; wait_slot waits until a tile ID has been pushed into a
+// claimed slot and, with CP_FLAG_FENCE_RELEASE, makes the producers' stores
+// of that tile's inputs visible.  wait_slot returns the tile ID, or kDone
+// when the queue is exhausted or the run has failed.  A worker claims its
+// next slot while its current tile's epilogue runs, so the claim's round
+// trip is hidden and a slot waits at most one epilogue for its worker.
 //
 // Forward progress: slots of a queue are handed out in order and pushes
 // claim slots in order, so if some tile is ready, every slot of its queue
 // below it is claimed and filled without waiting.  Take an unfinished tile
 // of lowest layer: its producers are finished, so it has been pushed, and
-// the workers of its queue reach it.  Every queue has workers and all
-// workers are resident (the grid fits the device at once), so no wait lasts
-// forever for a well-formed dependency table; if the device is shared and
-// some workers are not resident, the watchdog ends the run with a timeout.
-__device__ uint32_t prologue(const ChainArgs &a, int q) {
-    if (ld_relaxed(a.ctl + kCtlStatus) != 0) return kDone;
-    const uint32_t t = __hip_atomic_fetch_add(a.ctl + ctl_head(q), 1u, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
+// the workers of its queue reach it (a worker holding that slot is at worst
+// finishing a tile whose own inputs are complete).  Every queue has workers
+// and all workers are resident (the grid fits the device at once), so no
+// wait lasts forever for a well-formed dependency table; if the device is
+// shared and some workers are not resident, the watchdog ends the run with
+// a timeout.
+__device__ uint32_t take_ticket(const ChainArgs &a, int q) {
+    if (ld_relaxed(a.ctl + kCtlStatus) != 0) return kDone;  // >= any queue size
+    return __hip_atomic_fetch_add(a.ctl + ctl_head(q), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ uint32_t wait_slot(const ChainArgs &a, int q, uint32_t t) {
     if (t >= (uint32_t)a.qsize[q]) return kDone;
     const uint32_t *slot = a.queue + a.qbase[q] + t;
     const uint64_t t0 = wall_clock64();
@@ -605,21 +622,25 @@ __device__ void publish(const ChainArgs &a, uint32_t id, int l) {
             cq = owner_queue(next, (int)c, a.nq);
         }
         if (!__ballot(ready)) continue;
+        // Lane q counts this batch's ready consumers of queue q and every
+        // ready lane its rank among them; then lanes 0 .. nq-1 claim their
+        // queues' slots in one atomic instruction (one round trip for all
+        // queues), and each ready lane stores its ID into its claimed slot.
+        const uint64_t below = (1ull << lane) - 1ull;
+        uint32_t cnt = 0, rank = 0;
         for (int q = 0; q < a.nq; ++q) {
-            const uint64_t mask = __ballot(ready && cq == q);
-            if (!mask) continue;
-            const int leader = __ffsll((unsigned long long)mask) - 1;
-            uint32_t base = 0;
-            if (lane == leader)
-                base = __hip_atomic_fetch_add(a.ctl + ctl_tail(q), (uint32_t)__popcll(mask),
-                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            base = __shfl(base, leader);
-            if (ready && cq == q) {
-                const uint32_t rank = (uint32_t)__popcll(mask & ((1ull << lane) - 1ull));
-                __hip_atomic_store(a.queue + a.qbase[q] + base + rank, c, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            }
+            const uint64_t m = __ballot(ready && cq == q);
+            if (lane == q) cnt = (uint32_t)__popcll(m);
+            if (cq == q) rank = (uint32_t)__popcll(m & below);
         }
+        uint32_t base = 0;
+        if (lane < a.nq && cnt)
+            base = __hip_atomic_fetch_add(a.ctl + ctl_tail(lane), cnt, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+        base = __shfl(base, cq);
+        if (ready)
+            __hip_atomic_store(a.queue + a.qbase[cq] + base + rank, c, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -655,11 +676,16 @@ __device__ void reset_copy(const ChainArgs &a, uint32_t *queue, uint32_t *ctl, i
     }
     if (blockIdx.x == 0 && threadIdx.x < kMaxQueues) {
         const int q = threadIdx.x;
-        ctl[ctl_head(q)] = 0;
+        // slots 0 .. (workers of queue q) - 1 are handed out statically
+        ctl[ctl_head(q)] = q < a.nq ? (uint32_t)((a.nworkers - q + a.nq - 1) / a.nq) : 0u;
         ctl[ctl_tail(q)] = q < a.nq ? (uint32_t)a.qfirst[q] : 0u;
         if (q == 0) ctl[kCtlStatus] = 0;
     }
 }
+
+// Lane 0 of wave 1: the worker's scheduler (takes tickets, polls slots),
+// while wave 0 is the publisher.
+constexpr int kSchedLane = 64;
 
 // Persistent worker: loop prologue -> tile body -> publish until its queue
 // (blockIdx.x mod nq, so that workgroups dispatched round-robin over the
@@ -676,19 +702,27 @@ __global__ void __launch_bounds__(Body::NT) worker_kernel(ChainArgs a) {
     Stages<Body>::get(stg);
     volatile uint32_t *slot = reinterpret_cast<volatile uint32_t *>(stg[0]);
     const int q = (int)(blockIdx.x % (unsigned)a.nq);
+    const bool sched = threadIdx.x == kSchedLane;
     reset_copy(a, a.nxt_queue, a.nxt_ctl, a.nxt_score, a.nxt_deq_count, a.nxt_trace);
+    // first slot without an atomic: the r-th worker of queue q owns slot r
+    // (the reset set each head past the workers' count)
+    uint32_t ticket = blockIdx.x / (unsigned)a.nq;
     for (;;) {
-        if (threadIdx.x == 0) *slot = prologue(a, q);
+        if (sched) *slot = wait_slot(a, q, ticket);
         __syncthreads();
         const uint32_t id = *slot;
         __syncthreads();
         if (id >= (uint32_t)a.T) break;
         int l, i, j;
         decode(a, id, l, i, j);
-        Body::run(a.layer[l], i, j, stg);
+        Body::run(a.layer[l], i, j, stg, [&] {
+            if (sched) ticket = take_ticket(a, q);
+        });
         if (a.trace && threadIdx.x == 0) a.trace[4 * (size_t)id + 2] = wall_clock64();
+        // after publish's opening barrier wave 0 releases the tile while the
+        // scheduler lane (wave 1) already waits for the next one
         if (l + 1 < a.L) publish(a, id, l);
-        __syncthreads();
+        else __syncthreads();
     }
 }
 
@@ -701,7 +735,7 @@ __global__ void __launch_bounds__(Body::NT) layer_kernel(ChainArgs a, int l, int
     const LayerDesc &d = a.layer[l];
     const int t = blockIdx.x;
     const int i = rb0 + t / d.nbn, j = t % d.nbn;
-    Body::run(d, i, j, stg);
+    Body::run(d, i, j, stg, [] {});
 }
 
 // Reset of the current copy (at plan time, for both copies).
