@@ -59,7 +59,9 @@ int check_shape(int64_t M, int32_t L, const int64_t *widths, int32_t tile_m, int
     int64_t tiles = 0;
     for (int l = 0; l <= L; ++l) {
         if (widths[l] <= 0) return fail(CP_ERR_SHAPE, "widths[%d] = %lld must be positive", l, (long long)widths[l]);
-        if (widths[l] > (int64_t)1 << 30) return fail(CP_ERR_SHAPE, "widths[%d] too large", l);
+        if (widths[l] > (int64_t)1 << 22)
+            return fail(CP_ERR_SHAPE, "widths[%d] = %lld exceeds 2^22 (tile-relative 32-bit offsets)", l,
+                        (long long)widths[l]);
         if (l < L && k_step > 0 && widths[l] % k_step)
             return fail(CP_ERR_SHAPE, "contraction length widths[%d] = %lld is not a multiple of %d", l,
                         (long long)widths[l], k_step);

@@ -64,6 +64,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 template <int U>
 using ic = std::integral_constant<int, U>;
 
+// Fourth word of a raw (stride 0) buffer resource on gfx9-family parts:
+// 32-bit data format, so untyped dword loads are in range.
+constexpr int kRsrcWord3 = 0x00020000;
+
 // ----------------------------------------------------------------------------
 // bf16 tile body: C[BM x BN] tile (i, j) of A[M][K] . W[K][N], slabs of BK
 // (32 or 64) k, S-stage LDS pipeline.
@@ -140,7 +144,13 @@ struct Bf16Body {
         uint16_t *__restrict__ C = static_cast<uint16_t *>(d.C);
         const int K = d.K, N = d.N;
         const int row0 = i * BM, col0 = j * BN;
-        const int tid = threadIdx.x, lane = tid & 63;
+        // Per-lane addresses derive from tid; the empty asm makes them
+        // opaque to the compiler, so a persistent worker recomputes them per
+        // tile instead of keeping them live across its tile loop (which
+        // would exceed the register budget and spill).
+        int tid = threadIdx.x;
+        __asm__ volatile("" : "+v"(tid));
+        const int lane = tid & 63;
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int wm = wave / WGN, wn = wave % WGN;
 
@@ -153,6 +163,13 @@ struct Bf16Body {
                 for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.0f;
 
         // per-lane source offsets (elements) of this wave's direct loads
+        // Direct loads are buffer loads: a wave-uniform buffer resource (in
+        // SGPRs; base = the tile's first A row, or W row k0, advanced per
+        // slab, size = the bytes the slab may touch) plus a 32-bit per-lane
+        // byte offset that is fixed for the whole tile.  No 64-bit per-lane
+        // address arithmetic, half the address registers, and a lane outside
+        // the resource reads zeros instead of faulting.  Offsets stay below
+        // 2^32 because rows are at most 2^22 elements (checked at plan time).
         uint32_t a_off[A_PW], b_off[B_PW];
 #pragma unroll
         for (int q = 0; q < A_PW; ++q) {
@@ -166,26 +183,33 @@ struct Bf16Body {
                 r = 2 * L + (v >> 2);
                 c = v & 3;
             }
-            a_off[q] = (uint32_t)((row0 + r) * K + c * 8);
+            a_off[q] = (uint32_t)r * (uint32_t)K * 2u + (uint32_t)c * 16u;
         }
 #pragma unroll
         for (int q = 0; q < B_PW; ++q) {
             const int o = (q * NW + wave) * 1024 + lane * 16;  // byte in the W region
             const int k = o / RB, c = ((o % RB) >> 4) ^ fb(o / RB);
-            b_off[q] = (uint32_t)(k * N + col0 + c * 8);
+            b_off[q] = (uint32_t)k * (uint32_t)N * 2u + (uint32_t)c * 16u;
         }
+        char *const a_base = reinterpret_cast<char *>(const_cast<uint16_t *>(A) + (size_t)row0 * K);
+        char *const w_base = reinterpret_cast<char *>(const_cast<uint16_t *>(W) + col0);
+        const uint32_t a_bytes = (uint32_t)BM * (uint32_t)K * 2u;             // the tile's A rows
+        const uint32_t w_bytes = (uint32_t)(BK - 1) * (uint32_t)N * 2u + BN * 2u;  // one W slab
 
         auto issue = [&](char *As, int k0) {
             char *Bs = As + A_BYTES;
+            const __amdgpu_buffer_rsrc_t ra =
+                __builtin_amdgcn_make_buffer_rsrc(a_base + (size_t)k0 * 2, 0, (int)(a_bytes - 2u * k0), kRsrcWord3);
 #pragma unroll
             for (int q = 0; q < A_PW; ++q)
-                __builtin_amdgcn_global_load_lds(A + a_off[q] + k0,
-                                                 (lds_void_t *)(As + (q * NW + wave) * 1024), 16, 0, 0);
-            const uint16_t *Wk = W + (size_t)k0 * N;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t *)(As + (q * NW + wave) * 1024), 16,
+                                                         a_off[q], 0, 0, 0);
+            const __amdgpu_buffer_rsrc_t rw =
+                __builtin_amdgcn_make_buffer_rsrc(w_base + (size_t)k0 * N * 2, 0, (int)w_bytes, kRsrcWord3);
 #pragma unroll
             for (int q = 0; q < B_PW; ++q)
-                __builtin_amdgcn_global_load_lds(Wk + b_off[q],
-                                                 (lds_void_t *)(Bs + (q * NW + wave) * 1024), 16, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t *)(Bs + (q * NW + wave) * 1024), 16,
+                                                         b_off[q], 0, 0, 0);
         };
 
         // fragment addresses that do not depend on the stage or k step
@@ -445,9 +469,10 @@ struct F32Body {
         lstore(stg[0]);
         __syncthreads();
         for (int ks = 0; ks < nk; ++ks) {
+            char *cur = (ks & 1) ? stg[1] : stg[0], *nxt = (ks & 1) ? stg[0] : stg[1];  // no dynamic indexing
             if (ks + 1 < nk) gload((ks + 1) * BK);
-            compute(stg[ks & 1]);
-            if (ks + 1 < nk) lstore(stg[(ks + 1) & 1]);
+            compute(cur);
+            if (ks + 1 < nk) lstore(nxt);
             __syncthreads();
         }
         before_epilogue();
@@ -710,7 +735,9 @@ __global__ void __launch_bounds__(Body::NT) worker_kernel(ChainArgs a) {
     for (;;) {
         if (sched) *slot = wait_slot(a, q, ticket);
         __syncthreads();
-        const uint32_t id = *slot;
+        // the broadcast ID is uniform; saying so keeps the layer descriptor
+        // and the buffer resources derived from it in scalar registers
+        const uint32_t id = __builtin_amdgcn_readfirstlane(*slot);
         __syncthreads();
         if (id >= (uint32_t)a.T) break;
         int l, i, j;
