@@ -221,6 +221,7 @@ def compare_modes(plan, step, stream, cfg, tile, reps, torch, tuning):
         tag = "cold" if cold else "warm"
         out[f"pipelined_{tag}"] = timed("pipelined", 0, cold)
         out[f"sequential_{tag}"] = timed("sequential", 0, cold)
+        out[f"spatial_{tag}"] = timed("spatial", 0, cold)
         best = None
         sweep = {}
         for m in tuning.chunk_sweep(cfg.M, tile[0]):

@@ -54,6 +54,10 @@ typedef struct cp_chain cp_chain; /* opaque plan */
 #define CP_MODE_PIPELINED 0  /* one persistent launch, tile dependencies   */
 #define CP_MODE_SEQUENTIAL 1 /* one launch per layer (kernel boundaries)   */
 #define CP_MODE_MICROBATCH 2 /* M split into chunks over two streams       */
+#define CP_MODE_SPATIAL 3    /* one persistent launch per layer; layer l on CU
+                                set l mod 2 (two disjoint CU-masked streams),
+                                linked by the same scoreboard through one queue
+                                per layer                                      */
 
 /* status codes */
 #define CP_OK 0

@@ -48,8 +48,9 @@ def run_modes(rt, X, Ws, dtype, tile, acts=None, flags=0, modes=("pipelined", "s
                       microbatch_rows=(mb_rows or tile[0]) if mode == "microbatch" else 0)
                 st = c.stats()
                 assert st["status"] == 0, st
-                if mode == "pipelined":
+                if mode in ("pipelined", "spatial"):
                     check_invariants(st, flags)
+                if mode == "pipelined":
                     stats = st
                 y = ch.to_host(dY, dtype)
                 if rep == 0:
@@ -100,13 +101,14 @@ def test_c1_fp32_parity_all_modes(rt):
     X, Ws = gen.config_inputs(cfg)
     say("c1: fp32 128x512x512x512, tile", cfg.tile)
     out, st = run_modes(rt, X, Ws, cfg.dtype, cfg.tile, flags=all_flags(),
-                        modes=("pipelined", "sequential", "microbatch"), mb_rows=64, reps=3)
+                        modes=("pipelined", "sequential", "microbatch", "spatial"), mb_rows=64, reps=3)
     ref = oracle.chain(X, Ws, cfg.dtype)
     err = oracle.rel_err(as_values(out["pipelined"], cfg.dtype), ref)
     say("c1 rel err", err, "stats", st)
     assert err <= TOL[gen.F32]
     assert same_bits(out["pipelined"], out["sequential"])
     assert same_bits(out["pipelined"], out["microbatch"])
+    assert same_bits(out["pipelined"], out["spatial"])
     assert st["n_tiles"] == 32 and st["n_edges"] == 128
 
 
@@ -124,13 +126,14 @@ def test_bf16_small_parity(rt, tile):
     say("bf16 small", tile, M, widths)
     X, Ws = gen.chain_inputs(M, widths, gen.BF16, 1.0, (1 / np.sqrt(320), 1 / np.sqrt(3 * bn)), 50)
     out, st = run_modes(rt, X, Ws, gen.BF16, tile, flags=all_flags(),
-                        modes=("pipelined", "sequential", "microbatch"), mb_rows=bm)
+                        modes=("pipelined", "sequential", "microbatch", "spatial"), mb_rows=bm)
     ref = oracle.chain(X, Ws, gen.BF16)
     err = oracle.rel_err(as_values(out["pipelined"], gen.BF16), ref)
     say("rel err", err)
     assert err <= TOL[gen.BF16]
     assert same_bits(out["pipelined"], out["sequential"])
     assert same_bits(out["pipelined"], out["microbatch"])
+    assert same_bits(out["pipelined"], out["spatial"])
 
 
 @pytest.mark.parametrize("release", ["write-through", "fence"])
@@ -150,10 +153,11 @@ def test_signed_permutation_chain_exact_with_poison(rt, dtype, release):
     Ws = [gen.signed_permutation(n, 61 + l, dtype, scale_pow2=s) for l, s in enumerate((1, -2, 0))]
     say("perm chain", dtype, tile, M, n, release)
     out, st = run_modes(rt, X, Ws, dtype, tile, flags=all_flags() | f["DELAY"] | extra,
-                        modes=("pipelined", "sequential"), reps=3)
+                        modes=("pipelined", "sequential", "spatial"), reps=3)
     ref = oracle.chain(X, Ws, dtype)
     assert np.array_equal(as_values(out["pipelined"], dtype), ref)
     assert np.array_equal(as_values(out["sequential"], dtype), ref)
+    assert np.array_equal(as_values(out["spatial"], dtype), ref)
 
 
 def test_gelu_chain_small(rt):
@@ -184,11 +188,13 @@ def test_edge_shapes(rt, case):
     stds = tuple(1 / np.sqrt(widths[l]) for l in range(L))
     X, Ws = gen.chain_inputs(M, widths, gen.BF16, 1.0, stds, 80)
     say("edge", name)
-    out, st = run_modes(rt, X, Ws, gen.BF16, tile, flags=all_flags())
+    out, st = run_modes(rt, X, Ws, gen.BF16, tile, flags=all_flags(),
+                        modes=("pipelined", "sequential", "spatial"))
     ref = oracle.chain(X, Ws, gen.BF16)
     err = oracle.rel_err(as_values(out["pipelined"], gen.BF16), ref)
     assert err <= TOL[gen.BF16], err
     assert same_bits(out["pipelined"], out["sequential"])
+    assert same_bits(out["pipelined"], out["spatial"])
 
 
 def test_many_tiles_many_waves(rt):
@@ -219,6 +225,30 @@ def test_pipelined_repeats_alternate_state(rt, coop):
     assert oracle.rel_err(as_values(out["pipelined"], gen.BF16), ref) <= TOL[gen.BF16]
 
 
+def test_pipelined_and_spatial_alternate(rt):
+    """The two protocol modes use different queue layouts; switching between
+    them resets the state copy for the new layout first.  Every run in an
+    alternating sequence meets the invariants and gives the same bits."""
+    torch, ch = rt["torch"], rt["chain"]
+    M, widths = 512, (256, 512, 384, 256)
+    X, Ws = gen.chain_inputs(M, widths, gen.BF16, 1.0, (1 / 16, 1 / np.sqrt(512), 1 / np.sqrt(384)), 84)
+    dX, dW = ch.to_device(X, gen.BF16), [ch.to_device(w, gen.BF16) for w in Ws]
+    say("alternating pipelined / spatial")
+    ref = None
+    with ch.Chain(M, widths, gen.BF16, 64, 128, flags=all_flags()) as c:
+        for mode in ("pipelined", "spatial", "spatial", "pipelined", "pipelined", "spatial", "pipelined"):
+            dY = torch.full((M, widths[-1]), float("nan"), dtype=torch.bfloat16, device="cuda")
+            c.run(dX, dW, dY, mode=mode)
+            st = c.stats()
+            check_invariants(st, all_flags())
+            y = ch.to_host(dY, gen.BF16)
+            if ref is None:
+                ref = y
+            assert same_bits(y, ref), mode
+    err = oracle.rel_err(as_values(ref, gen.BF16), oracle.chain(X, Ws, gen.BF16))
+    assert err <= TOL[gen.BF16]
+
+
 def test_rejects_bad_shapes_on_device(rt):
     nat = rt["nat"]
     with pytest.raises(nat.CpError) as e:
@@ -246,6 +276,10 @@ def test_watchdog_timeout_is_reported(rt):
         st = c.stats(check=False)
         assert st["status"] == nat.CP_ERR_TIMEOUT and st["tail"] == st["n_tiles"] - 1, st
         assert st["bad_dequeues"] == 1, st   # only the starved tile is never dequeued
+        # spatial mode waits on the same never-ready tile and times out too
+        c.run(dX, dW, dY, mode="spatial")
+        st = c.stats(check=False)
+        assert st["status"] == nat.CP_ERR_TIMEOUT and st["tail"] == st["n_tiles"] - 1, st
         # the plan is reusable afterwards in the other modes
         c.run(dX, dW, dY, mode="sequential")
         assert c.stats()["status"] == 0

@@ -9,7 +9,7 @@ from . import native as nat
 
 DTYPES = {nat.CP_F32: torch.float32, nat.CP_BF16: torch.bfloat16}
 MODES = {"pipelined": nat.CP_MODE_PIPELINED, "sequential": nat.CP_MODE_SEQUENTIAL,
-         "microbatch": nat.CP_MODE_MICROBATCH}
+         "microbatch": nat.CP_MODE_MICROBATCH, "spatial": nat.CP_MODE_SPATIAL}
 
 
 class Chain:

@@ -120,9 +120,27 @@ struct cp_chain {
     int device = 0;
     const cp::Variant *var = nullptr;
     TileGraph g;
-    int n_workers = 0;
-    int nq = 1;                        // work-queues (one per XCD, at most kMaxQueues)
-    int32_t qbase[cp::kMaxQueues] = {}, qsize[cp::kMaxQueues] = {}, qfirst[cp::kMaxQueues] = {};
+    int n_workers = 0;                 // pipelined mode's persistent grid
+    // Queue layouts: kXcd (pipelined mode) has one queue per XCD, a tile in
+    // the queue of its column panel mod 8, and worker b serves queue b mod 8;
+    // kLayer (spatial mode) has one queue per layer, served by that layer's
+    // own launch.
+    struct Layout {
+        int nq = 1;
+        int32_t qbase[cp::kMaxQueues] = {}, qsize[cp::kMaxQueues] = {}, qfirst[cp::kMaxQueues] = {};
+        int32_t qworkers[cp::kMaxQueues] = {};
+        uint32_t *d_qinit = nullptr;   // initial queue image
+    } lay[2];
+    int copy_layout[2] = {0, 0};       // layout each per-run state copy was reset for
+    int last_layout = 0;
+    // spatial mode: two disjoint CU sets, layer l on set l mod 2, each set
+    // with its own CU-masked stream (made on first use)
+    int n_sets = 1;
+    uint32_t cu_mask[2][8] = {};
+    int sp_workers[CP_MAX_LAYERS] = {};
+    int sp_cus[2] = {};
+    hipStream_t sp_stream[2] = {};
+    hipEvent_t sp_join[2] = {};
     bool coop = false;                 // cooperative launch of the persistent grid
     // device state (one allocation) and intermediates.  The per-run state
     // (scoreboard, queues, counters, debug counts, trace) has two copies: a
@@ -130,7 +148,6 @@ struct cp_chain {
     // which the next run uses, so no reset launch precedes the worker grid.
     char *state = nullptr;
     int32_t *d_indeg = nullptr, *d_dep_off = nullptr, *d_dep_ids = nullptr;
-    uint32_t *d_qinit = nullptr;
     int32_t *d_score[2] = {};
     uint32_t *d_queue[2] = {}, *d_ctl[2] = {}, *d_deq[2] = {};
     uint64_t *d_trace[2] = {};
@@ -176,6 +193,10 @@ void release(cp_chain *p) {
     for (auto &s : p->side)
         if (s) (void)hipStreamDestroy(s);
     if (p->cap) (void)hipStreamDestroy(p->cap);
+    for (auto &st : p->sp_stream)
+        if (st) (void)hipStreamDestroy(st);
+    for (auto &e : p->sp_join)
+        if (e) (void)hipEventDestroy(e);
     if (p->ev_fork) (void)hipEventDestroy(p->ev_fork);
     for (auto &e : p->ev_join)
         if (e) (void)hipEventDestroy(e);
@@ -191,11 +212,9 @@ void release(cp_chain *p) {
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 cp::ChainArgs make_args(const cp_chain *p, const void *X, const void *const *W, void *Y, int copy,
-                        int32_t mode = CP_MODE_PIPELINED) {
+                        int32_t mode = CP_MODE_PIPELINED, int layout = 0, int fixed_queue = -1) {
     cp::ChainArgs a;
     memset(&a, 0, sizeof a);
-    const size_t es = p->dtype == CP_BF16 ? 2 : 4;
-    (void)es;
     for (int l = 0; l < p->L; ++l) {
         cp::LayerDesc &d = a.layer[l];
         d.A = l == 0 ? X : p->inter[l - 1];
@@ -205,21 +224,26 @@ cp::ChainArgs make_args(const cp_chain *p, const void *X, const void *const *W, 
         d.N = (int32_t)p->widths[l + 1];
         d.nbn = p->g.nbn[l];
         d.act = p->acts[l];
-        d.coherent = (mode == CP_MODE_PIPELINED && l + 1 < p->L && !(p->flags & CP_FLAG_FENCE_RELEASE)) ? 1 : 0;
+        d.coherent = ((mode == CP_MODE_PIPELINED || mode == CP_MODE_SPATIAL) && l + 1 < p->L &&
+                      !(p->flags & CP_FLAG_FENCE_RELEASE)) ? 1 : 0;
         d.tile_off = p->g.layer_off[l];
         d.ntiles = p->g.layer_off[l + 1] - p->g.layer_off[l];
     }
     a.L = p->L;
     a.T = p->g.T;
     a.flags = p->flags;
-    a.nq = p->nq;
-    a.nworkers = p->n_workers;
+    const cp_chain::Layout &ly = p->lay[layout];
+    a.nq = ly.nq;
+    a.nworkers = fixed_queue >= 0 ? p->sp_workers[fixed_queue] : p->n_workers;
+    a.fixed_queue = fixed_queue;
+    a.queue_by_layer = layout == 1 ? 1 : 0;
     for (int q = 0; q < cp::kMaxQueues; ++q) {
-        a.qbase[q] = p->qbase[q];
-        a.qsize[q] = p->qsize[q];
-        a.qfirst[q] = p->qfirst[q];
+        a.qbase[q] = ly.qbase[q];
+        a.qsize[q] = ly.qsize[q];
+        a.qfirst[q] = ly.qfirst[q];
+        a.qworkers[q] = ly.qworkers[q];
     }
-    a.qinit = p->d_qinit;
+    a.qinit = ly.d_qinit;
     const int c = copy, n = copy ^ 1;
     a.queue = p->d_queue[c];
     a.ctl = p->d_ctl[c];
@@ -348,6 +372,7 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
     const size_t o_doff = off;    off = align_up(off + (T + 1) * 4, 256);
     const size_t o_dids = off;    off = align_up(off + E * 4, 256);
     const size_t o_qinit = off;   off = align_up(off + T * 4, 256);
+    const size_t o_qinit2 = off;  off = align_up(off + T * 4, 256);
     int rc2 = [&]() -> int {
         CP_HIP(hipMalloc(&p->state, off));
         for (int c = 0; c < 2; ++c) {
@@ -360,7 +385,8 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
         p->d_indeg = reinterpret_cast<int32_t *>(p->state + o_indeg);
         p->d_dep_off = reinterpret_cast<int32_t *>(p->state + o_doff);
         p->d_dep_ids = reinterpret_cast<int32_t *>(p->state + o_dids);
-        p->d_qinit = reinterpret_cast<uint32_t *>(p->state + o_qinit);
+        p->lay[0].d_qinit = reinterpret_cast<uint32_t *>(p->state + o_qinit);
+        p->lay[1].d_qinit = reinterpret_cast<uint32_t *>(p->state + o_qinit2);
         CP_HIP(hipMemset(p->state, 0, off));
         CP_HIP(hipMemcpy(p->d_indeg, g.indeg.data(), T * 4, hipMemcpyHostToDevice));
         CP_HIP(hipMemcpy(p->d_dep_off, g.dep_off.data(), (T + 1) * 4, hipMemcpyHostToDevice));
@@ -370,8 +396,6 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
             p->inter_bytes[l] = (size_t)M * (size_t)widths[l + 1] * es;
             CP_HIP(hipMalloc(&p->inter[l], p->inter_bytes[l]));
         }
-        for (auto &s : p->side) CP_HIP(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
-        CP_HIP(hipStreamCreateWithFlags(&p->cap, hipStreamNonBlocking));
         CP_HIP(hipEventCreateWithFlags(&p->ev_fork, hipEventDisableTiming));
         for (auto &e : p->ev_join) CP_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
         CP_HIP(hipEventCreate(&p->ev_start));
@@ -391,25 +415,66 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
         }
         // one queue per XCD; a tile belongs to the queue of its column panel
         int xcds = 8;
-        p->nq = std::max(1, std::min({cp::kMaxQueues, xcds, p->n_workers}));
-        std::vector<std::vector<uint32_t>> first(p->nq);
-        std::vector<int32_t> size(p->nq, 0);
+        cp_chain::Layout &lx = p->lay[0];
+        lx.nq = std::max(1, std::min({cp::kMaxQueues, xcds, p->n_workers}));
+        std::vector<std::vector<uint32_t>> first(lx.nq);
+        std::vector<int32_t> size(lx.nq, 0);
         for (int l = 0; l < n_layers; ++l)
             for (int32_t t = g.layer_off[l]; t < g.layer_off[l + 1]; ++t) {
-                const int q = ((t - g.layer_off[l]) % g.nbn[l]) % p->nq;
+                const int q = ((t - g.layer_off[l]) % g.nbn[l]) % lx.nq;
                 ++size[q];
                 if (l == 0) first[q].push_back((uint32_t)t);  // row-block-major
             }
         std::vector<uint32_t> qinit((size_t)g.T, cp::kEmpty);
         int32_t base = 0;
-        for (int q = 0; q < p->nq; ++q) {
-            p->qbase[q] = base;
-            p->qsize[q] = size[q];
-            p->qfirst[q] = (int32_t)first[q].size();
+        for (int q = 0; q < lx.nq; ++q) {
+            lx.qbase[q] = base;
+            lx.qsize[q] = size[q];
+            lx.qfirst[q] = (int32_t)first[q].size();
+            lx.qworkers[q] = (p->n_workers - q + lx.nq - 1) / lx.nq;
             std::copy(first[q].begin(), first[q].end(), qinit.begin() + base);
             base += size[q];
         }
-        CP_HIP(hipMemcpy(p->d_qinit, qinit.data(), T * 4, hipMemcpyHostToDevice));
+        CP_HIP(hipMemcpy(lx.d_qinit, qinit.data(), T * 4, hipMemcpyHostToDevice));
+        // spatial layout: queue l holds layer l's tiles (layer 0 pre-filled,
+        // row-block-major).  Layer l runs on CU set l mod 2, so every layer's
+        // CUs are disjoint from those of the layers it feeds and consumes;
+        // the sets are sized by the flops of their layers.  The driver
+        // accepts masks made of contiguous CU ranges (an every-other-CU mask
+        // is refused), so each 32-CU word of the mask is cut into two
+        // contiguous runs of CU pairs.  Only two CU-masked streams are used:
+        // each takes a hardware queue of its own, and a process has few.
+        cp_chain::Layout &ll = p->lay[1];
+        ll.nq = n_layers;
+        p->n_sets = n_layers > 1 ? 2 : 1;
+        double fl[2] = {0.0, 0.0};
+        for (int l = 0; l < n_layers; ++l) fl[l % 2] += (double)widths[l] * (double)widths[l + 1];
+        for (int w = 0; w < 8 && 32 * w < cus; ++w) {
+            const int pairs = std::min(32, cus - 32 * w) / 2;
+            int p0 = pairs;
+            if (p->n_sets == 2) {
+                if (pairs < 2) return fail(CP_ERR_UNSUPPORTED, "spatial mode: too few CUs per mask word");
+                p0 = std::min(pairs - 1, std::max(1, (int)(fl[0] / (fl[0] + fl[1]) * pairs + 0.5)));
+            }
+            for (int b = 0; b < 2 * pairs; ++b) {
+                const int set = b < 2 * p0 ? 0 : 1;
+                p->cu_mask[set][w] |= 1u << b;
+                ++p->sp_cus[set];
+            }
+        }
+        for (int l = 0; l < n_layers; ++l) {
+            const int32_t nt = g.layer_off[l + 1] - g.layer_off[l];
+            p->sp_workers[l] = std::max(1, std::min(per_cu * p->sp_cus[l % 2], nt));
+            ll.qbase[l] = g.layer_off[l];
+            ll.qsize[l] = nt;
+            ll.qfirst[l] = l == 0 ? nt : 0;
+            ll.qworkers[l] = p->sp_workers[l];
+        }
+        std::vector<uint32_t> qinit2((size_t)g.T, cp::kEmpty);
+        for (int32_t t = 0; t < g.P1; ++t) qinit2[t] = (uint32_t)t;
+        CP_HIP(hipMemcpy(ll.d_qinit, qinit2.data(), T * 4, hipMemcpyHostToDevice));
+        for (auto &s : p->side) CP_HIP(hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
+        CP_HIP(hipStreamCreateWithFlags(&p->cap, hipStreamNonBlocking));
         // both copies of the per-run state start reset
         for (int c = 0; c < 2; ++c) CP_HIP(cp::launch_reset(make_args(p, nullptr, nullptr, nullptr, c), p->cap));
         CP_HIP(hipStreamSynchronize(p->cap));
@@ -498,6 +563,41 @@ int find_replay(cp_chain *p, const cp::ChainArgs &a, const void *X, const void *
 
 }  // namespace
 
+namespace {
+
+// Spatial mode: layer l's persistent grid on CU set l mod 2 (a CU-masked
+// stream), forked from and joined back into `s`.  Layer l's workers serve
+// only queue l; producers push consumers into the next layer's queue.
+// Disjoint CU sets make it deadlock-free: a consumer grid spinning on its
+// queue never holds its producer's CUs.
+int enqueue_spatial(cp_chain *p, const void *X, const void *const *W, void *Y, hipStream_t s) {
+    for (int k = 0; k < p->n_sets; ++k) {
+        if (p->sp_stream[k]) continue;
+        const hipError_t e = hipExtStreamCreateWithCUMask(&p->sp_stream[k], 8, p->cu_mask[k]);  // 8 words
+        if (e != hipSuccess) {
+            p->sp_stream[k] = nullptr;
+            return fail(CP_ERR_UNSUPPORTED, "spatial mode: the runtime refused a CU-masked stream (%s); "
+                        "each needs a hardware queue of its own", hipGetErrorString(e));
+        }
+        CP_HIP(hipEventCreateWithFlags(&p->sp_join[k], hipEventDisableTiming));
+    }
+    CP_HIP(hipEventRecord(p->ev_fork, s));
+    for (int k = 0; k < p->n_sets; ++k) CP_HIP(hipStreamWaitEvent(p->sp_stream[k], p->ev_fork, 0));
+    // in layer order: a layer only ever queues behind an earlier layer on its
+    // set, which never waits on it, so the in-order streams cannot deadlock
+    for (int l = 0; l < p->L; ++l) {
+        const cp::ChainArgs a = make_args(p, X, W, Y, p->cur, CP_MODE_SPATIAL, 1, l);
+        CP_HIP(p->var->launch_worker(a, p->sp_workers[l], false, p->sp_stream[l % 2]));
+    }
+    for (int k = 0; k < p->n_sets; ++k) {
+        CP_HIP(hipEventRecord(p->sp_join[k], p->sp_stream[k]));
+        CP_HIP(hipStreamWaitEvent(s, p->sp_join[k], 0));
+    }
+    return CP_OK;
+}
+
+}  // namespace
+
 int cp_chain_run(cp_chain *p, const void *X, const void *const *W, void *Y, void *stream,
                  int32_t mode, int64_t microbatch_rows) {
     g_last_error.clear();
@@ -505,7 +605,8 @@ int cp_chain_run(cp_chain *p, const void *X, const void *const *W, void *Y, void
     if (!X || !W || !Y) return fail(CP_ERR_INVALID_ARG, "X, W or Y is NULL");
     for (int l = 0; l < p->L; ++l)
         if (!W[l]) return fail(CP_ERR_INVALID_ARG, "W[%d] is NULL", l);
-    if (mode != CP_MODE_PIPELINED && mode != CP_MODE_SEQUENTIAL && mode != CP_MODE_MICROBATCH)
+    if (mode != CP_MODE_PIPELINED && mode != CP_MODE_SEQUENTIAL && mode != CP_MODE_MICROBATCH &&
+        mode != CP_MODE_SPATIAL)
         return fail(CP_ERR_INVALID_ARG, "mode %d", mode);
     if (mode == CP_MODE_MICROBATCH) {
         if (microbatch_rows <= 0 || microbatch_rows % p->tile_m || p->M % microbatch_rows)
@@ -521,8 +622,8 @@ int cp_chain_run(cp_chain *p, const void *X, const void *const *W, void *Y, void
     CP_HIP(hipStreamIsCapturing(s, &cs));
     if (cs != hipStreamCaptureStatusNone) {
         // recorded into the caller's graph: kernels only, no timing events
-        if (mode == CP_MODE_PIPELINED)
-            return fail(CP_ERR_UNSUPPORTED, "pipelined mode cannot be captured into a graph (its per-run state alternates between two copies)");
+        if (mode == CP_MODE_PIPELINED || mode == CP_MODE_SPATIAL)
+            return fail(CP_ERR_UNSUPPORTED, "pipelined and spatial modes cannot be captured into a graph (their per-run state alternates between two copies)");
         if (p->flags & CP_FLAG_POISON)
             for (int l = 0; l + 1 < p->L; ++l) CP_HIP(cp::launch_poison(p->inter[l], p->inter_bytes[l], p->dtype, s));
         return enqueue_layers(p, a, mode, microbatch_rows, s);
@@ -534,9 +635,22 @@ int cp_chain_run(cp_chain *p, const void *X, const void *const *W, void *Y, void
     if (timed) CP_HIP(hipEventRecord(p->ev_start, s));
     if (p->flags & CP_FLAG_POISON)
         for (int l = 0; l + 1 < p->L; ++l) CP_HIP(cp::launch_poison(p->inter[l], p->inter_bytes[l], p->dtype, s));
-    if (mode == CP_MODE_PIPELINED) {
+    if (mode == CP_MODE_PIPELINED || mode == CP_MODE_SPATIAL) {
+        // The state copy must have been reset for this mode's queue layout
+        // (the previous run's workers reset it for their own layout).
+        const int layout = mode == CP_MODE_SPATIAL ? 1 : 0;
+        if (p->copy_layout[p->cur] != layout)
+            CP_HIP(cp::launch_reset(make_args(p, nullptr, nullptr, nullptr, p->cur, mode, layout), s));
         if (timed && (p->flags & CP_FLAG_POISON)) CP_HIP(hipEventRecord(p->ev_kernel, s));
-        CP_HIP(p->var->launch_worker(a, p->n_workers, p->coop, s));
+        if (mode == CP_MODE_PIPELINED) {
+            CP_HIP(p->var->launch_worker(a, p->n_workers, p->coop, s));
+        } else {
+            int rc = enqueue_spatial(p, X, W, Y, s);
+            if (rc) return rc;
+        }
+        p->copy_layout[p->cur] = layout;
+        p->copy_layout[p->cur ^ 1] = layout;  // reset by this run's workers
+        p->last_layout = layout;
         p->last_copy = p->cur;
         p->cur ^= 1;
     } else {
@@ -579,7 +693,7 @@ int cp_chain_stats(cp_chain *p, cp_chain_stats_t *out) {
     out->n_first = p->g.P1;
     out->n_edges = p->g.E;
     out->n_workers = p->n_workers;
-    out->n_queues = p->nq;
+    out->n_queues = p->lay[0].nq;
     out->tile_m = p->tile_m;
     out->tile_n = p->tile_n;
     out->bad_dequeues = -1;
@@ -599,7 +713,7 @@ int cp_chain_stats(cp_chain *p, cp_chain_stats_t *out) {
             out->last_kernel_ms = ms;
         }
     }
-    if (p->last_mode != CP_MODE_PIPELINED) return CP_OK;
+    if (p->last_mode != CP_MODE_PIPELINED && p->last_mode != CP_MODE_SPATIAL) return CP_OK;
 
     const size_t T = (size_t)p->g.T;
     uint32_t ctl[cp::kCtlWords];
@@ -610,13 +724,14 @@ int cp_chain_stats(cp_chain *p, cp_chain_stats_t *out) {
     CP_HIP(hipMemcpy(score.data(), p->d_score[c], T * 4, hipMemcpyDeviceToHost));
     CP_HIP(hipMemcpy(queue.data(), p->d_queue[c], T * 4, hipMemcpyDeviceToHost));
     out->status = (int32_t)ctl[cp::kCtlStatus];
-    out->n_queues = p->nq;
+    const cp_chain::Layout &ly = p->lay[p->last_layout];
+    out->n_queues = ly.nq;
     out->queues_drained = 1;
-    for (int q = 0; q < p->nq; ++q) {
+    for (int q = 0; q < ly.nq; ++q) {
         const uint32_t h = ctl[cp::ctl_head(q)], t = ctl[cp::ctl_tail(q)];
         out->head += h;
         out->tail += t;
-        if (t != (uint32_t)p->qsize[q] || h < (uint32_t)p->qsize[q]) out->queues_drained = 0;
+        if (t != (uint32_t)ly.qsize[q] || h < (uint32_t)ly.qsize[q]) out->queues_drained = 0;
     }
     int32_t nz = 0;
     for (size_t t = 0; t < T; ++t) nz += score[t] != 0;

@@ -47,7 +47,11 @@ struct ChainArgs {
     int32_t T;           // tiles over all layers
     uint32_t flags;      // CP_FLAG_*
     int32_t nq;          // queues in use (1..kMaxQueues)
-    int32_t nworkers;    // persistent workers (grid size); worker b serves queue b mod nq
+    int32_t nworkers;    // persistent workers (grid size)
+    int32_t fixed_queue;     // >= 0: every worker of this launch serves that queue (spatial
+                             // mode), else worker b serves queue b mod nq
+    int32_t queue_by_layer;  // 1: a tile's queue is its layer (spatial); 0: column panel mod nq
+    int32_t qworkers[kMaxQueues];  // workers serving each queue; they own its first slots
     int32_t qbase[kMaxQueues];   // first slot of each queue in `queue`
     int32_t qsize[kMaxQueues];   // tiles owned by each queue
     int32_t qfirst[kMaxQueues];  // of which first-layer tiles (pre-filled)

@@ -644,7 +644,7 @@ __device__ void publish(const ChainArgs &a, uint32_t id, int l) {
             const int old = __hip_atomic_fetch_sub(a.score + c, 1, __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_AGENT);
             ready = (old == 1);
-            cq = owner_queue(next, (int)c, a.nq);
+            cq = a.queue_by_layer ? l + 1 : owner_queue(next, (int)c, a.nq);
         }
         if (!__ballot(ready)) continue;
         // Lane q counts this batch's ready consumers of queue q and every
@@ -702,7 +702,7 @@ __device__ void reset_copy(const ChainArgs &a, uint32_t *queue, uint32_t *ctl, i
     if (blockIdx.x == 0 && threadIdx.x < kMaxQueues) {
         const int q = threadIdx.x;
         // slots 0 .. (workers of queue q) - 1 are handed out statically
-        ctl[ctl_head(q)] = q < a.nq ? (uint32_t)((a.nworkers - q + a.nq - 1) / a.nq) : 0u;
+        ctl[ctl_head(q)] = q < a.nq ? (uint32_t)a.qworkers[q] : 0u;
         ctl[ctl_tail(q)] = q < a.nq ? (uint32_t)a.qfirst[q] : 0u;
         if (q == 0) ctl[kCtlStatus] = 0;
     }
@@ -726,12 +726,12 @@ __global__ void __launch_bounds__(Body::NT) worker_kernel(ChainArgs a) {
     char *stg[5];
     Stages<Body>::get(stg);
     volatile uint32_t *slot = reinterpret_cast<volatile uint32_t *>(stg[0]);
-    const int q = (int)(blockIdx.x % (unsigned)a.nq);
+    const int q = a.fixed_queue >= 0 ? a.fixed_queue : (int)(blockIdx.x % (unsigned)a.nq);
     const bool sched = threadIdx.x == kSchedLane;
     reset_copy(a, a.nxt_queue, a.nxt_ctl, a.nxt_score, a.nxt_deq_count, a.nxt_trace);
     // first slot without an atomic: the r-th worker of queue q owns slot r
     // (the reset set each head past the workers' count)
-    uint32_t ticket = blockIdx.x / (unsigned)a.nq;
+    uint32_t ticket = a.fixed_queue >= 0 ? blockIdx.x : blockIdx.x / (unsigned)a.nq;
     for (;;) {
         if (sched) *slot = wait_slot(a, q, ticket);
         __syncthreads();

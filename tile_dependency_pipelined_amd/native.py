@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(PKG, "libcpchain.so")
 
 CP_F32, CP_BF16 = 0, 1
 CP_ACT_NONE, CP_ACT_GELU_TANH = 0, 1
-CP_MODE_PIPELINED, CP_MODE_SEQUENTIAL, CP_MODE_MICROBATCH = 0, 1, 2
+CP_MODE_PIPELINED, CP_MODE_SEQUENTIAL, CP_MODE_MICROBATCH, CP_MODE_SPATIAL = 0, 1, 2, 3
 CP_OK = 0
 CP_ERR_INVALID_ARG = -1
 CP_ERR_SHAPE = -2
