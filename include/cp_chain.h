@@ -100,6 +100,8 @@ typedef struct cp_chain cp_chain; /* opaque plan */
  * last_run_ms / last_kernel_ms); each event stalls the stream for a few
  * microseconds, so untimed plans record only one completion event */
 #define CP_FLAG_TIMING 256u
+/* never split a layer's k range (see cp_chain_plan: split-K) */
+#define CP_FLAG_NO_SPLIT 512u
 
 #define CP_MAX_LAYERS 8
 
@@ -107,7 +109,7 @@ typedef struct cp_chain cp_chain; /* opaque plan */
 typedef struct cp_chain_stats_t {
     int32_t status;          /* CP_OK, or CP_ERR_TIMEOUT if a worker's wait expired        */
     int32_t mode;            /* mode of the last run                                      */
-    int32_t n_tiles;         /* T: tiles over all layers                                  */
+    int32_t n_tiles;         /* T: work items over all layers (tiles, or tiles x nsplit)  */
     int32_t n_first;         /* P1: tiles of layer 1 (pre-filled into the queue)          */
     int32_t n_edges;         /* E: dependency edges = scoreboard decrements per run       */
     int32_t n_workers;       /* persistent workgroups launched (pipelined mode)           */
@@ -124,6 +126,8 @@ typedef struct cp_chain_stats_t {
                                 (plans built with CP_FLAG_TIMING; -1 otherwise)           */
     double last_kernel_ms;   /* pipelined with CP_FLAG_POISON: the persistent launch alone
                                 (poison fills excluded); otherwise same as last_run_ms    */
+    int32_t nonzero_arrivals;/* split-K tiles whose arrival count did not end at 0        */
+    int32_t nsplit[CP_MAX_LAYERS]; /* split-K items per tile of each layer (1 = no split) */
 } cp_chain_stats_t;
 
 /*
@@ -143,6 +147,15 @@ typedef struct cp_chain_stats_t {
  * of the GEMM (§III-A; review, "Circularity Check") -- uploads it, allocates the
  * scoreboard, queue, intermediates C_1..C_{L-1} (M x N_l each) and sizes the
  * persistent grid from occupancy.  Needs a HIP device (CP_ERR_NO_DEVICE).
+ * Every width must be at most 2^22.
+ * Split-K: a bf16 layer with fewer tiles than the persistent grid holds is
+ * split along k into power-of-two ranges (items) until it fills the grid,
+ * keeping at least 16 k-slabs per item and, beyond layer 1, ranges made of
+ * whole producer tiles; an item then waits only on the producer tiles of its
+ * own k range.  Items store fp32 partials into a plan-owned workspace and
+ * the last item of a tile to finish sums them in split order, so results do
+ * not depend on timing and all modes agree bit for bit.  CP_FLAG_NO_SPLIT
+ * turns it off; cp_chain_stats reports the split of each layer.
  */
 int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *widths,
                   int32_t dtype, int32_t tile_m, int32_t tile_n, const int32_t *acts,

@@ -69,6 +69,7 @@ def check_invariants(st, flags):
     assert st["tail"] == T, st
     assert st["head"] >= T, st
     assert st["queues_drained"] == 1, st
+    assert st["nonzero_arrivals"] == 0, st
     if flags & rt_flags()["DEBUG"]:
         assert st["bad_dequeues"] == 0, st
     if flags & rt_flags()["TRACE"]:
@@ -247,6 +248,34 @@ def test_pipelined_and_spatial_alternate(rt):
             assert same_bits(y, ref), mode
     err = oracle.rel_err(as_values(ref, gen.BF16), oracle.chain(X, Ws, gen.BF16))
     assert err <= TOL[gen.BF16]
+
+
+@pytest.mark.parametrize("acts", [(gen.ACT_NONE, gen.ACT_NONE), (gen.ACT_GELU_TANH, gen.ACT_NONE)],
+                         ids=["plain", "gelu"])
+def test_split_k_layers(rt, acts):
+    """Layers with fewer tiles than the worker grid holds are split along k:
+    every item stores an fp32 partial and the last to arrive sums them in
+    split order and runs the epilogue (GeLU included).  All four modes give
+    the same bits, the arrival counters end at 0, and the result matches the
+    oracle; with CP_FLAG_NO_SPLIT it matches the oracle too."""
+    nat = rt["nat"]
+    M, widths = 128, (4096, 2048, 512)
+    X, Ws = gen.chain_inputs(M, widths, gen.BF16, 1.0, (1 / 64, 1 / np.sqrt(2048)), 85)
+    say("split-K chain", M, widths, acts)
+    out, st = run_modes(rt, X, Ws, gen.BF16, (128, 128), acts=list(acts), flags=all_flags(),
+                        modes=("pipelined", "sequential", "microbatch", "spatial"), mb_rows=128, reps=2)
+    say("nsplit", st["nsplit"], "items", st["n_tiles"])
+    assert st["nsplit"][0] > 1 and st["nsplit"][1] > 1, st["nsplit"]
+    ref = oracle.chain(X, Ws, gen.BF16, acts=list(acts))
+    err = oracle.rel_err(as_values(out["pipelined"], gen.BF16), ref)
+    say("split rel err", err)
+    assert err <= TOL[gen.BF16]
+    for m in ("sequential", "microbatch", "spatial"):
+        assert same_bits(out["pipelined"], out[m]), m
+    out2, st2 = run_modes(rt, X, Ws, gen.BF16, (128, 128), acts=list(acts),
+                          flags=all_flags() | nat.CP_FLAG_NO_SPLIT, modes=("pipelined",))
+    assert st2["nsplit"][:2] == [1, 1]
+    assert oracle.rel_err(as_values(out2["pipelined"], gen.BF16), ref) <= TOL[gen.BF16]
 
 
 def test_rejects_bad_shapes_on_device(rt):

@@ -43,10 +43,12 @@ int fail(int code, const char *fmt, ...) {
                         #call, hipGetErrorString(e_), __FILE__, __LINE__);               \
     } while (0)
 
-// Tile graph of a chain: flat IDs, in-degree template and CSR out-edges.
+// Tile graph of a chain: flat work-item IDs, in-degree template and CSR
+// out-edges.  Without split-K an item is a tile; with nsplit[l] > 1 each
+// tile of layer l is nsplit[l] consecutive items over disjoint k ranges.
 struct TileGraph {
     int32_t T = 0, P1 = 0, E = 0;
-    std::vector<int32_t> layer_off, nbn, indeg, dep_off, dep_ids;
+    std::vector<int32_t> layer_off, nbn, nsplit, indeg, dep_off, dep_ids;
 };
 
 int check_shape(int64_t M, int32_t L, const int64_t *widths, int32_t tile_m, int32_t tile_n,
@@ -78,14 +80,20 @@ int check_shape(int64_t M, int32_t L, const int64_t *widths, int32_t tile_m, int
 
 // Dependency table (§III-A): tile (l+1, i, j) waits on all N_l / tile_n tiles
 // (l, i, k) of row-block i, because its A operand is that whole row-block.
+// With split-K, item s of tile (l+1, i, j) reads only columns
+// [s N_l / ns, (s + 1) N_l / ns) of that row-block, so it waits on just the
+// producer tiles of those columns.  A producer tile's out-edges sit on its
+// first item: whichever of its items completes the tile releases them.
 void build_graph(int64_t M, int32_t L, const int64_t *widths, int32_t tile_m, int32_t tile_n,
-                 TileGraph &g) {
+                 const int32_t *nsplit, TileGraph &g) {
     const int32_t nrb = (int32_t)(M / tile_m);
     g.layer_off.assign(L + 1, 0);
     g.nbn.assign(L, 0);
+    g.nsplit.assign(L, 1);
     for (int l = 0; l < L; ++l) {
         g.nbn[l] = (int32_t)(widths[l + 1] / tile_n);
-        g.layer_off[l + 1] = g.layer_off[l] + nrb * g.nbn[l];
+        g.nsplit[l] = nsplit ? nsplit[l] : 1;
+        g.layer_off[l + 1] = g.layer_off[l] + nrb * g.nbn[l] * g.nsplit[l];
     }
     g.T = g.layer_off[L];
     g.P1 = g.layer_off[1];
@@ -93,19 +101,40 @@ void build_graph(int64_t M, int32_t L, const int64_t *widths, int32_t tile_m, in
     g.dep_off.assign(g.T + 1, 0);
     for (int l = 0; l < L; ++l)
         for (int32_t t = g.layer_off[l]; t < g.layer_off[l + 1]; ++t) {
-            if (l > 0) g.indeg[t] = g.nbn[l - 1];
-            g.dep_off[t + 1] = g.dep_off[t] + (l + 1 < L ? g.nbn[l + 1] : 0);
+            const int32_t split = (t - g.layer_off[l]) % g.nsplit[l];
+            if (l > 0) g.indeg[t] = g.nbn[l - 1] / g.nsplit[l];
+            g.dep_off[t + 1] = g.dep_off[t] + (l + 1 < L && split == 0 ? g.nbn[l + 1] : 0);
         }
     g.E = g.dep_off[g.T];
     g.dep_ids.assign(g.E, 0);
-    for (int l = 0; l + 1 < L; ++l)
+    for (int l = 0; l + 1 < L; ++l) {
+        const int32_t per_split = g.nbn[l] / g.nsplit[l + 1];  // producer tiles per consumer k range
         for (int32_t i = 0; i < nrb; ++i)
             for (int32_t k = 0; k < g.nbn[l]; ++k) {
-                const int32_t p = g.layer_off[l] + i * g.nbn[l] + k;
+                const int32_t p = g.layer_off[l] + (i * g.nbn[l] + k) * g.nsplit[l];
                 int32_t e = g.dep_off[p];
                 for (int32_t j = 0; j < g.nbn[l + 1]; ++j)
-                    g.dep_ids[e++] = g.layer_off[l + 1] + i * g.nbn[l + 1] + j;
+                    g.dep_ids[e++] = g.layer_off[l + 1] + (i * g.nbn[l + 1] + j) * g.nsplit[l + 1] + k / per_split;
             }
+    }
+}
+
+// Split-K factor per layer: a layer with fewer tiles than the persistent grid
+// holds is split into power-of-two k ranges until it fills the grid, keeping
+// at least 16 slabs per item and (beyond layer 0) k ranges that are whole
+// producer tiles.  fp32 layers are never split.
+void choose_splits(int64_t M, int32_t L, const int64_t *widths, int32_t tile_m, int32_t tile_n, int32_t dtype,
+                   int32_t k_step, int32_t capacity, bool allow, int32_t *ns) {
+    const int64_t nrb = M / tile_m;
+    for (int l = 0; l < L; ++l) {
+        ns[l] = 1;
+        if (!allow || dtype != CP_BF16) continue;
+        const int64_t tiles = nrb * (widths[l + 1] / tile_n), slabs = widths[l] / k_step;
+        const int64_t prod_tiles = l > 0 ? widths[l] / tile_n : 0;
+        while (tiles * 2 * ns[l] <= capacity && slabs % (2 * ns[l]) == 0 && slabs / (2 * ns[l]) >= 16 &&
+               (l == 0 || prod_tiles % (2 * ns[l]) == 0))
+            ns[l] *= 2;
+    }
 }
 
 }  // namespace
@@ -149,6 +178,9 @@ struct cp_chain {
     char *state = nullptr;
     int32_t *d_indeg = nullptr, *d_dep_off = nullptr, *d_dep_ids = nullptr;
     int32_t *d_score[2] = {};
+    uint32_t *d_arrive[3] = {};        // split-K arrival counts: run copies 0, 1 and the baselines'
+    int32_t nsplit[CP_MAX_LAYERS] = {};
+    float *ws[CP_MAX_LAYERS] = {};     // split-K partial tiles per split layer
     uint32_t *d_queue[2] = {}, *d_ctl[2] = {}, *d_deq[2] = {};
     uint64_t *d_trace[2] = {};
     int cur = 0;                       // copy of the next pipelined run
@@ -205,6 +237,8 @@ void release(cp_chain *p) {
     if (p->ev_stop) (void)hipEventDestroy(p->ev_stop);
     for (auto &b : p->inter)
         if (b) (void)hipFree(b);
+    for (auto &b : p->ws)
+        if (b) (void)hipFree(b);
     if (p->state) (void)hipFree(p->state);
     delete p;
 }
@@ -228,6 +262,8 @@ cp::ChainArgs make_args(const cp_chain *p, const void *X, const void *const *W, 
                       !(p->flags & CP_FLAG_FENCE_RELEASE)) ? 1 : 0;
         d.tile_off = p->g.layer_off[l];
         d.ntiles = p->g.layer_off[l + 1] - p->g.layer_off[l];
+        d.nsplit = p->g.nsplit[l];
+        d.ws = p->ws[l];
     }
     a.L = p->L;
     a.T = p->g.T;
@@ -248,6 +284,9 @@ cp::ChainArgs make_args(const cp_chain *p, const void *X, const void *const *W, 
     a.queue = p->d_queue[c];
     a.ctl = p->d_ctl[c];
     a.score = p->d_score[c];
+    const bool protocol = mode == CP_MODE_PIPELINED || mode == CP_MODE_SPATIAL;
+    a.arrive = protocol ? p->d_arrive[c] : p->d_arrive[2];
+    a.nxt_arrive = p->d_arrive[n];
     a.nxt_queue = p->d_queue[n];
     a.nxt_ctl = p->d_ctl[n];
     a.nxt_score = p->d_score[n];
@@ -291,7 +330,7 @@ int cp_chain_tile_graph(int64_t M, int32_t n_layers, const int64_t *widths, int3
     if (rc) return rc;
     TileGraph g;
     try {
-        build_graph(M, n_layers, widths, tile_m, tile_n, g);
+        build_graph(M, n_layers, widths, tile_m, tile_n, nullptr, g);
     } catch (const std::bad_alloc &) {
         return fail(CP_ERR_OOM, "host allocation failed");
     }
@@ -322,7 +361,8 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
             if (acts[l] != CP_ACT_NONE && acts[l] != CP_ACT_GELU_TANH)
                 return fail(CP_ERR_INVALID_ARG, "acts[%d] = %d", l, acts[l]);
     const uint32_t known = CP_FLAG_DEBUG | CP_FLAG_TRACE | CP_FLAG_POISON | CP_FLAG_DELAY_INJECT | CP_FLAG_STARVE_LAST |
-                           CP_FLAG_EAGER | CP_FLAG_COOPERATIVE | CP_FLAG_FENCE_RELEASE | CP_FLAG_TIMING;
+                           CP_FLAG_EAGER | CP_FLAG_COOPERATIVE | CP_FLAG_FENCE_RELEASE | CP_FLAG_TIMING |
+                           CP_FLAG_NO_SPLIT;
     if (flags & ~known) return fail(CP_ERR_INVALID_ARG, "unknown flags 0x%x", flags & ~known);
     if ((flags & CP_FLAG_STARVE_LAST) && n_layers < 2)
         return fail(CP_ERR_INVALID_ARG, "CP_FLAG_STARVE_LAST needs at least two layers");
@@ -349,8 +389,15 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
         return code;
     };
     if (hipGetDevice(&p->device) != hipSuccess) return bail(fail(CP_ERR_NO_DEVICE, "hipGetDevice failed"));
+    int per_cu = 0, cus = 0;
+    if (var->occupancy(&per_cu) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device) != hipSuccess)
+        return bail(fail(CP_ERR_HIP, "occupancy / CU count query failed"));
+    if (per_cu < 1) return bail(fail(CP_ERR_UNSUPPORTED, "kernel cannot be resident (occupancy 0)"));
+    choose_splits(M, n_layers, widths, tile_m, tile_n, dtype, var->k_step, per_cu * cus,
+                  !(flags & CP_FLAG_NO_SPLIT), p->nsplit);
     try {
-        build_graph(M, n_layers, widths, tile_m, tile_n, p->g);
+        build_graph(M, n_layers, widths, tile_m, tile_n, p->nsplit, p->g);
     } catch (const std::bad_alloc &) {
         return bail(fail(CP_ERR_OOM, "host allocation failed"));
     }
@@ -360,7 +407,10 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
     // one device allocation for all protocol state
     const size_t T = (size_t)g.T, E = (size_t)std::max(g.E, 1);
     size_t off = 0;
-    size_t o_ctl[2], o_score[2], o_queue[2], o_deq[2], o_trace[2];
+    size_t o_ctl[2], o_score[2], o_queue[2], o_deq[2], o_trace[2], o_arrive[3];
+    for (int c = 0; c < 3; ++c) {
+        o_arrive[c] = off; off = align_up(off + T * 4, 256);  // two run copies + the baselines'
+    }
     for (int c = 0; c < 2; ++c) {
         o_ctl[c] = off;   off = align_up(off + cp::kCtlWords * 4, 256);
         o_score[c] = off; off = align_up(off + T * 4, 256);
@@ -382,6 +432,7 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
             p->d_deq[c] = reinterpret_cast<uint32_t *>(p->state + o_deq[c]);
             p->d_trace[c] = (flags & CP_FLAG_TRACE) ? reinterpret_cast<uint64_t *>(p->state + o_trace[c]) : nullptr;
         }
+        for (int c = 0; c < 3; ++c) p->d_arrive[c] = reinterpret_cast<uint32_t *>(p->state + o_arrive[c]);
         p->d_indeg = reinterpret_cast<int32_t *>(p->state + o_indeg);
         p->d_dep_off = reinterpret_cast<int32_t *>(p->state + o_doff);
         p->d_dep_ids = reinterpret_cast<int32_t *>(p->state + o_dids);
@@ -396,15 +447,14 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
             p->inter_bytes[l] = (size_t)M * (size_t)widths[l + 1] * es;
             CP_HIP(hipMalloc(&p->inter[l], p->inter_bytes[l]));
         }
+        for (int l = 0; l < n_layers; ++l)  // split-K partials: one fp32 tile per item
+            if (p->nsplit[l] > 1)
+                CP_HIP(hipMalloc(&p->ws[l], (size_t)(g.layer_off[l + 1] - g.layer_off[l]) * tile_m * tile_n * 4));
         CP_HIP(hipEventCreateWithFlags(&p->ev_fork, hipEventDisableTiming));
         for (auto &e : p->ev_join) CP_HIP(hipEventCreateWithFlags(&e, hipEventDisableTiming));
         CP_HIP(hipEventCreate(&p->ev_start));
         CP_HIP(hipEventCreate(&p->ev_kernel));
         CP_HIP(hipEventCreate(&p->ev_stop));
-        int per_cu = 0, cus = 0;
-        CP_HIP(var->occupancy(&per_cu));
-        CP_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device));
-        if (per_cu < 1) return fail(CP_ERR_UNSUPPORTED, "kernel cannot be resident (occupancy 0)");
         p->n_workers = std::max(1, std::min(per_cu * cus, g.T));
         if (flags & CP_FLAG_COOPERATIVE) {
             int coop_ok = 0;
@@ -421,9 +471,9 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
         std::vector<int32_t> size(lx.nq, 0);
         for (int l = 0; l < n_layers; ++l)
             for (int32_t t = g.layer_off[l]; t < g.layer_off[l + 1]; ++t) {
-                const int q = ((t - g.layer_off[l]) % g.nbn[l]) % lx.nq;
+                const int q = ((t - g.layer_off[l]) % (g.nbn[l] * g.nsplit[l])) % lx.nq;
                 ++size[q];
-                if (l == 0) first[q].push_back((uint32_t)t);  // row-block-major
+                if (l == 0) first[q].push_back((uint32_t)t);  // row-block-major (then item order)
             }
         std::vector<uint32_t> qinit((size_t)g.T, cp::kEmpty);
         int32_t base = 0;
@@ -440,24 +490,25 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
         // row-block-major).  Layer l runs on CU set l mod 2, so every layer's
         // CUs are disjoint from those of the layers it feeds and consumes;
         // the sets are sized by the flops of their layers.  The driver
-        // accepts masks made of contiguous CU ranges (an every-other-CU mask
-        // is refused), so each 32-CU word of the mask is cut into two
-        // contiguous runs of CU pairs.  Only two CU-masked streams are used:
-        // each takes a hardware queue of its own, and a process has few.
+        // accepts a mask only in whole groups of 8 CUs (measured: 4-CU runs
+        // and every-other-CU masks are refused), so each 32-CU word of the
+        // mask is cut into two contiguous runs of whole octets.  Only two
+        // CU-masked streams are used: each takes a hardware queue of its own,
+        // and a process has few.
         cp_chain::Layout &ll = p->lay[1];
         ll.nq = n_layers;
         p->n_sets = n_layers > 1 ? 2 : 1;
         double fl[2] = {0.0, 0.0};
         for (int l = 0; l < n_layers; ++l) fl[l % 2] += (double)widths[l] * (double)widths[l + 1];
         for (int w = 0; w < 8 && 32 * w < cus; ++w) {
-            const int pairs = std::min(32, cus - 32 * w) / 2;
-            int p0 = pairs;
+            const int octs = std::min(32, cus - 32 * w) / 8;
+            int o0 = octs;
             if (p->n_sets == 2) {
-                if (pairs < 2) return fail(CP_ERR_UNSUPPORTED, "spatial mode: too few CUs per mask word");
-                p0 = std::min(pairs - 1, std::max(1, (int)(fl[0] / (fl[0] + fl[1]) * pairs + 0.5)));
+                if (octs < 2) return fail(CP_ERR_UNSUPPORTED, "spatial mode: too few CUs per mask word");
+                o0 = std::min(octs - 1, std::max(1, (int)(fl[0] / (fl[0] + fl[1]) * octs + 0.5)));
             }
-            for (int b = 0; b < 2 * pairs; ++b) {
-                const int set = b < 2 * p0 ? 0 : 1;
+            for (int b = 0; b < 8 * octs; ++b) {
+                const int set = b < 8 * o0 ? 0 : 1;
                 p->cu_mask[set][w] |= 1u << b;
                 ++p->sp_cus[set];
             }
@@ -698,6 +749,7 @@ int cp_chain_stats(cp_chain *p, cp_chain_stats_t *out) {
     out->tile_n = p->tile_n;
     out->bad_dequeues = -1;
     out->order_violations = -1;
+    for (int l = 0; l < CP_MAX_LAYERS; ++l) out->nsplit[l] = l < p->L ? p->g.nsplit[l] : 0;
     out->last_run_ms = -1.0;
     out->last_kernel_ms = -1.0;
     if (!p->ran) return CP_OK;
@@ -736,6 +788,11 @@ int cp_chain_stats(cp_chain *p, cp_chain_stats_t *out) {
     int32_t nz = 0;
     for (size_t t = 0; t < T; ++t) nz += score[t] != 0;
     out->nonzero_scores = nz;
+    std::vector<uint32_t> arr(T);
+    CP_HIP(hipMemcpy(arr.data(), p->d_arrive[c], T * 4, hipMemcpyDeviceToHost));
+    nz = 0;
+    for (size_t t = 0; t < T; ++t) nz += arr[t] != 0;
+    out->nonzero_arrivals = nz;
     std::vector<uint8_t> seen(T, 0);
     bool perm = true;
     for (size_t t = 0; t < T; ++t) {

@@ -36,8 +36,11 @@ struct LayerDesc {
     int32_t nbn;       // N / tile_n: tiles per row-block
     int32_t act;       // CP_ACT_*
     int32_t tile_off;  // flat ID of this layer's first tile
-    int32_t ntiles;    // (M / tile_m) * nbn
+    int32_t ntiles;    // work items of this layer: (M / tile_m) * nbn * nsplit
     int32_t coherent;  // store C at agent scope (write-through of the XCD's L2)
+    int32_t nsplit;    // split-K: items per output tile (1 = no split); item s of a
+                       // tile covers k in [s K / nsplit, (s + 1) K / nsplit)
+    float *ws;         // nsplit > 1: fp32 partial tiles, one per item
 };
 
 // Everything one launch needs, passed by value as the kernel argument.
@@ -64,18 +67,22 @@ struct ChainArgs {
     const uint32_t *qinit;   // [T] initial queue contents (reset source)
     uint32_t *deq_count;     // [T] debug: dequeues per tile, or null
     uint64_t *trace;         // [4T] timestamps, or null
+    uint32_t *arrive;        // [T] split-K: items of a tile that finished (at its first item's
+                             // index); the last one sums the partials and resets it to 0
     // the other copy of the per-run state (queue, ctl, score, deq_count,
     // trace), used by the next pipelined run; this run's workers reset it
     uint32_t *nxt_queue, *nxt_ctl;
     int32_t *nxt_score;
     uint32_t *nxt_deq_count;
+    uint32_t *nxt_arrive;
     uint64_t *nxt_trace;
     uint64_t timeout_ticks;  // watchdog on a queue wait, 100 MHz ticks
 };
 
-// Queue that owns tile `id` of layer `l`: its column panel modulo nq.
+// Queue that owns work item `id` of layer `l`: (column panel x nsplit +
+// split) modulo nq, so the items of one tile spread over the queues.
 __host__ __device__ inline int owner_queue(const LayerDesc &d, int id, int nq) {
-    return ((id - d.tile_off) % d.nbn) % nq;
+    return ((id - d.tile_off) % (d.nbn * d.nsplit)) % nq;
 }
 
 // A compiled kernel variant (element type x tile shape).

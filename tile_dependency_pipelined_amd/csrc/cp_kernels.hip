@@ -135,10 +135,17 @@ struct Bf16Body {
     }
 
     // `before_epilogue` runs in every thread once the main loop is done (the
-    // worker takes its next ticket there).
-    template <class Hook>
-    __device__ __forceinline__ static void run(const LayerDesc &d, int i, int j, char *const *stg,
-                                               Hook &&before_epilogue) {
+    // worker takes its next ticket there).  Split-K (d.nsplit > 1): this
+    // item multiplies k in [split K / nsplit, (split + 1) K / nsplit) and
+    // stores an fp32 partial; the last item of the tile to arrive sums all
+    // partials in split order and runs the epilogue.  Returns whether this
+    // call completed the tile (stored C).
+    // SPLIT = false compiles the split-K path out (plans without a split
+    // layer use that instantiation: the extra live state would cost the
+    // persistent worker its scalar registers).
+    template <bool SPLIT, class Hook>
+    __device__ __forceinline__ static bool run(const LayerDesc &d, int i, int j, int split, uint32_t *arrive,
+                                               char *const *stg, Hook &&before_epilogue) {
         const uint16_t *__restrict__ A = static_cast<const uint16_t *>(d.A);
         const uint16_t *__restrict__ W = static_cast<const uint16_t *>(d.W);
         uint16_t *__restrict__ C = static_cast<uint16_t *>(d.C);
@@ -191,9 +198,13 @@ struct Bf16Body {
             const int k = o / RB, c = ((o % RB) >> 4) ^ fb(o / RB);
             b_off[q] = (uint32_t)k * (uint32_t)N * 2u + (uint32_t)c * 16u;
         }
-        char *const a_base = reinterpret_cast<char *>(const_cast<uint16_t *>(A) + (size_t)row0 * K);
-        char *const w_base = reinterpret_cast<char *>(const_cast<uint16_t *>(W) + col0);
-        const uint32_t a_bytes = (uint32_t)BM * (uint32_t)K * 2u;             // the tile's A rows
+        // this item's k range; integer division runs on the vector ALU, so
+        // say that the results are uniform (they feed the buffer resources)
+        const int kspan = SPLIT ? __builtin_amdgcn_readfirstlane(K / d.nsplit) : K;
+        const int kbeg = SPLIT ? __builtin_amdgcn_readfirstlane(split * kspan) : 0;
+        char *const a_base = reinterpret_cast<char *>(const_cast<uint16_t *>(A) + (size_t)row0 * K + kbeg);
+        char *const w_base = reinterpret_cast<char *>(const_cast<uint16_t *>(W) + (size_t)kbeg * N + col0);
+        const uint32_t a_bytes = (uint32_t)BM * (uint32_t)K * 2u - 2u * kbeg;  // the tile's A rows from kbeg
         const uint32_t w_bytes = (uint32_t)(BK - 1) * (uint32_t)N * 2u + BN * 2u;  // one W slab
 
         auto issue = [&](char *As, int k0) {
@@ -298,7 +309,7 @@ struct Bf16Body {
             }
         };
 
-        const int nk = K / BK;
+        const int nk = __builtin_amdgcn_readfirstlane(kspan / BK);
         // one pipeline step on the slab in stage u: slabs slab+1 .. slab+S-1
         // are in flight into the other stages; after the barrier stage u is
         // refilled with slab+S
@@ -330,6 +341,70 @@ struct Bf16Body {
         wait_vmcnt<0>();  // the trailing prefetches must land before the LDS is reused
         __syncthreads();
         before_epilogue();
+        const LayerDesc *dp = &d;
+
+        if (SPLIT && dp->nsplit > 1) {
+            // Partial tile, fragment-native layout [wave][fm][fn][h][lane][2]
+            // floats: every 8-byte store instruction writes 512 contiguous
+            // bytes.  Stored at agent scope (write-through of this XCD's L2);
+            // each wave waits for its stores before the barrier, so all of
+            // them are in memory before the arrival count is raised.
+            const int tile = i * dp->nbn + j;
+            float *ws = dp->ws + (size_t)(tile * dp->nsplit + split) * (BM * BN);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int h = 0; h < 8; ++h) {
+                        const uint64_t v = (uint64_t)__float_as_uint(acc[fm][fn][2 * h]) |
+                                           ((uint64_t)__float_as_uint(acc[fm][fn][2 * h + 1]) << 32);
+                        float *dst = ws + ((((wave * FM + fm) * FN + fn) * 8 + h) * 64 + lane) * 2;
+                        __hip_atomic_store(reinterpret_cast<uint64_t *>(dst), v, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                    }
+            wait_vmcnt<0>();
+            __syncthreads();
+            volatile uint32_t *word = reinterpret_cast<volatile uint32_t *>(stg[0]) + 1;
+            if (tid == 0)
+                *word = __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            const bool last = *word == (uint32_t)(dp->nsplit - 1);
+            __syncthreads();  // everyone has read the word before the LDS is reused
+            if (!last) return false;
+            // Last to arrive: every other item's partial is in memory.  Reset
+            // the count for the next run and sum the partials in split order
+            // (the same order whichever item arrives last), reading them at
+            // agent scope so that no cached line can be stale.
+            if (tid == 0) __hip_atomic_store(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const float *ws0 = dp->ws + (size_t)(tile * dp->nsplit) * (BM * BN);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                    for (int h = 0; h < 8; ++h) {
+                        const size_t o = ((((size_t)wave * FM + fm) * FN + fn) * 8 + h) * 128 + lane * 2;
+                        float s0 = 0.0f, s1 = 0.0f;
+                        for (int k = 0; k < dp->nsplit; ++k) {
+                            float v0, v1;
+                            if (k == split) {
+                                v0 = acc[fm][fn][2 * h];
+                                v1 = acc[fm][fn][2 * h + 1];
+                            } else {
+                                const uint64_t v = __hip_atomic_load(
+                                    reinterpret_cast<const uint64_t *>(ws0 + (size_t)k * (BM * BN) + o),
+                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                                v0 = __uint_as_float((uint32_t)v);
+                                v1 = __uint_as_float((uint32_t)(v >> 32));
+                            }
+                            s0 = k == 0 ? v0 : s0 + v0;
+                            s1 = k == 0 ? v1 : s1 + v1;
+                        }
+                        acc[fm][fn][2 * h] = s0;
+                        acc[fm][fn][2 * h + 1] = s1;
+                    }
+        }
 
         // Epilogue: activation on the fp32 accumulator, RNE to bf16, then the
         // tile goes through the (now idle) LDS stages so that every store
@@ -352,7 +427,7 @@ struct Bf16Body {
             if constexpr (S > 4) p = k == 4 ? stg[4] : p;
             return p;
         };
-        const int act = d.act;
+        const int act = dp->act;
         const int h8 = (lane >> 5) * 8;            // byte half of a 16-byte chunk
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
@@ -388,7 +463,7 @@ struct Bf16Body {
             return reinterpret_cast<const uint64_t *>(stage_of((it * RPI) / RPS) + (r % RPS) * (BN * 2) +
                                                       (((u >> 1) ^ (r % CPR)) << 4) + lds_u);
         };
-        if (__builtin_amdgcn_readfirstlane(d.coherent)) {
+        if (__builtin_amdgcn_readfirstlane(dp->coherent)) {
 #pragma unroll
             for (int it = 0; it < NI; ++it)
                 __hip_atomic_store(dst + (size_t)it * RPI * N / 4, *lds_at(it), __ATOMIC_RELAXED,
@@ -397,6 +472,7 @@ struct Bf16Body {
 #pragma unroll
             for (int it = 0; it < NI; ++it) dst[(size_t)it * RPI * N / 4] = *lds_at(it);
         }
+        return true;
     }
 };
 
@@ -411,11 +487,11 @@ struct F32Body {
     static constexpr int BP = BN + 4;  // padded W row ([k][n]), keeps 16-byte alignment
     static constexpr int STAGE = (BK * AP + BK * BP) * 4;
 
-    // `before_epilogue` runs in every thread once the main loop is done (the
-    // worker takes its next ticket there).
-    template <class Hook>
-    __device__ __forceinline__ static void run(const LayerDesc &d, int i, int j, char *const *stg,
-                                               Hook &&before_epilogue) {
+    // `before_epilogue` as in Bf16Body; no split-K (plans never split fp32
+    // layers), so every call completes its tile.
+    template <bool SPLIT, class Hook>
+    __device__ __forceinline__ static bool run(const LayerDesc &d, int i, int j, int /*split*/,
+                                               uint32_t * /*arrive*/, char *const *stg, Hook &&before_epilogue) {
         const float *__restrict__ A = static_cast<const float *>(d.A);
         const float *__restrict__ W = static_cast<const float *>(d.W);
         float *__restrict__ C = static_cast<float *>(d.C);
@@ -496,6 +572,7 @@ struct F32Body {
                 *reinterpret_cast<float4 *>(crow + n) = v;
             }
         }
+        return true;
     }
 };
 
@@ -669,12 +746,15 @@ __device__ void publish(const ChainArgs &a, uint32_t id, int l) {
     }
 }
 
-__device__ __forceinline__ void decode(const ChainArgs &a, uint32_t id, int &l, int &i, int &j) {
+__device__ __forceinline__ void decode(const ChainArgs &a, uint32_t id, int &l, int &i, int &j, int &split) {
     l = 0;
     while (l + 1 < a.L && (int)id >= a.layer[l + 1].tile_off) ++l;
-    const int loc = (int)id - a.layer[l].tile_off;
-    i = loc / a.layer[l].nbn;
-    j = loc - i * a.layer[l].nbn;
+    const LayerDesc &d = a.layer[l];
+    const int loc = (int)id - d.tile_off;
+    const int tile = __builtin_amdgcn_readfirstlane(loc / d.nsplit);
+    split = __builtin_amdgcn_readfirstlane(loc - tile * d.nsplit);
+    i = __builtin_amdgcn_readfirstlane(tile / d.nbn);
+    j = __builtin_amdgcn_readfirstlane(tile - i * d.nbn);
 }
 
 // ----------------------------------------------------------------------------
@@ -686,11 +766,12 @@ __device__ __forceinline__ void decode(const ChainArgs &a, uint32_t id, int &l, 
 // tiles in row-block-major order, EMPTY after), per-queue head = 0,
 // tail = pre-filled, status OK.  Grid-stride over the calling grid.
 __device__ void reset_copy(const ChainArgs &a, uint32_t *queue, uint32_t *ctl, int32_t *score,
-                           uint32_t *deq_count, uint64_t *trace) {
+                           uint32_t *deq_count, uint64_t *trace, uint32_t *arrive) {
     const int stride = gridDim.x * blockDim.x;
     for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < a.T; t += stride) {
         score[t] = a.indeg[t];
         queue[t] = a.qinit[t];
+        arrive[t] = 0;
         if (deq_count) deq_count[t] = 0;
         if (trace) {
             trace[4 * (size_t)t + 0] = 0;
@@ -721,14 +802,14 @@ constexpr int kSchedLane = 64;
 // run (nothing of this run reads it; the kernel boundary publishes it).  The
 // tile ID is broadcast through the first word of stage 0; the second barrier
 // guarantees every thread has read it before the body's loads reuse stage 0.
-template <class Body>
+template <class Body, bool SPLIT>
 __global__ void __launch_bounds__(Body::NT) worker_kernel(ChainArgs a) {
     char *stg[5];
     Stages<Body>::get(stg);
     volatile uint32_t *slot = reinterpret_cast<volatile uint32_t *>(stg[0]);
     const int q = a.fixed_queue >= 0 ? a.fixed_queue : (int)(blockIdx.x % (unsigned)a.nq);
     const bool sched = threadIdx.x == kSchedLane;
-    reset_copy(a, a.nxt_queue, a.nxt_ctl, a.nxt_score, a.nxt_deq_count, a.nxt_trace);
+    reset_copy(a, a.nxt_queue, a.nxt_ctl, a.nxt_score, a.nxt_deq_count, a.nxt_trace, a.nxt_arrive);
     // first slot without an atomic: the r-th worker of queue q owns slot r
     // (the reset set each head past the workers' count)
     uint32_t ticket = a.fixed_queue >= 0 ? blockIdx.x : blockIdx.x / (unsigned)a.nq;
@@ -740,33 +821,40 @@ __global__ void __launch_bounds__(Body::NT) worker_kernel(ChainArgs a) {
         const uint32_t id = __builtin_amdgcn_readfirstlane(*slot);
         __syncthreads();
         if (id >= (uint32_t)a.T) break;
-        int l, i, j;
-        decode(a, id, l, i, j);
-        Body::run(a.layer[l], i, j, stg, [&] {
+        int l, i, j, split;
+        decode(a, id, l, i, j, split);
+        const uint32_t first = id - (uint32_t)split;  // the tile's first item carries its edges
+        const bool done = Body::template run<SPLIT>(a.layer[l], i, j, split, a.arrive + first, stg, [&] {
             if (sched) ticket = take_ticket(a, q);
         });
         if (a.trace && threadIdx.x == 0) a.trace[4 * (size_t)id + 2] = wall_clock64();
         // after publish's opening barrier wave 0 releases the tile while the
-        // scheduler lane (wave 1) already waits for the next one
-        if (l + 1 < a.L) publish(a, id, l);
+        // scheduler lane (wave 1) already waits for the next one; a split-K
+        // item that did not complete its tile has nothing to release
+        if (done && l + 1 < a.L) publish(a, first, l);
         else __syncthreads();
     }
 }
 
 // One layer, one tile per workgroup, row-blocks [rb0, rb0 + nrb): the plain
 // kernel-boundary execution used by the sequential and micro-batched modes.
-template <class Body>
+template <class Body, bool SPLIT>
 __global__ void __launch_bounds__(Body::NT) layer_kernel(ChainArgs a, int l, int rb0) {
     char *stg[5];
     Stages<Body>::get(stg);
     const LayerDesc &d = a.layer[l];
+    const int per_rb = d.nbn * d.nsplit;  // items per row-block
     const int t = blockIdx.x;
-    const int i = rb0 + t / d.nbn, j = t % d.nbn;
-    Body::run(d, i, j, stg, [] {});
+    const int i = __builtin_amdgcn_readfirstlane(rb0 + t / per_rb), rem = t % per_rb;
+    const int j = __builtin_amdgcn_readfirstlane(rem / d.nsplit), split = __builtin_amdgcn_readfirstlane(rem % d.nsplit);
+    (void)Body::template run<SPLIT>(d, i, j, split, a.arrive + d.tile_off + (i * d.nbn + j) * d.nsplit, stg,
+                                    [] {});
 }
 
 // Reset of the current copy (at plan time, for both copies).
-__global__ void reset_kernel(ChainArgs a) { reset_copy(a, a.queue, a.ctl, a.score, a.deq_count, a.trace); }
+__global__ void reset_kernel(ChainArgs a) {
+    reset_copy(a, a.queue, a.ctl, a.score, a.deq_count, a.trace, a.arrive);
+}
 
 // Fill an intermediate with quiet NaN so that a premature read is visible.
 __global__ void poison_kernel(uint32_t *p, size_t words, uint32_t pattern) {
@@ -778,29 +866,44 @@ __global__ void poison_kernel(uint32_t *p, size_t words, uint32_t pattern) {
 // ----------------------------------------------------------------------------
 // Launchers and the variant table
 // ----------------------------------------------------------------------------
-template <class Body>
-hipError_t launch_worker_t(const ChainArgs &a, int grid, bool cooperative, hipStream_t s) {
+template <class Body, bool SPLIT>
+hipError_t launch_worker_s(const ChainArgs &a, int grid, bool cooperative, hipStream_t s) {
     if (!cooperative) {
-        hipLaunchKernelGGL(worker_kernel<Body>, dim3(grid), dim3(Body::NT), 0, s, a);
+        hipLaunchKernelGGL((worker_kernel<Body, SPLIT>), dim3(grid), dim3(Body::NT), 0, s, a);
         return hipGetLastError();
     }
     ChainArgs copy = a;
     void *args[] = {&copy};
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(worker_kernel<Body>), dim3(grid),
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(worker_kernel<Body, SPLIT>), dim3(grid),
                                       dim3(Body::NT), args, 0, s);
+}
+
+// Split-K instantiations exist only for bf16 bodies (fp32 layers never split).
+template <class Body>
+hipError_t launch_worker_t(const ChainArgs &a, int grid, bool cooperative, hipStream_t s) {
+    bool split = false;
+    for (int l = 0; l < a.L; ++l) split |= a.layer[l].nsplit > 1;
+    if constexpr (!std::is_same<Body, F32Body>::value)
+        if (split) return launch_worker_s<Body, true>(a, grid, cooperative, s);
+    return launch_worker_s<Body, false>(a, grid, cooperative, s);
 }
 
 template <class Body>
 hipError_t launch_layer_t(const ChainArgs &a, int l, int rb0, int nrb, hipStream_t s) {
-    const int grid = nrb * a.layer[l].nbn;
+    const int grid = nrb * a.layer[l].nbn * a.layer[l].nsplit;
     if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL(layer_kernel<Body>, dim3(grid), dim3(Body::NT), 0, s, a, l, rb0);
+    if constexpr (!std::is_same<Body, F32Body>::value)
+        if (a.layer[l].nsplit > 1) {
+            hipLaunchKernelGGL((layer_kernel<Body, true>), dim3(grid), dim3(Body::NT), 0, s, a, l, rb0);
+            return hipGetLastError();
+        }
+    hipLaunchKernelGGL((layer_kernel<Body, false>), dim3(grid), dim3(Body::NT), 0, s, a, l, rb0);
     return hipGetLastError();
 }
 
 template <class Body>
 hipError_t occupancy_t(int *blocks) {
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, worker_kernel<Body>, Body::NT, 0);
+    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, worker_kernel<Body, false>, Body::NT, 0);
 }
 
 // LDS stages per tile shape: as many as fit the occupancy each shape aims for

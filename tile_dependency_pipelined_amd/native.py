@@ -31,6 +31,7 @@ CP_FLAG_EAGER = 32
 CP_FLAG_COOPERATIVE = 64
 CP_FLAG_FENCE_RELEASE = 128
 CP_FLAG_TIMING = 256
+CP_FLAG_NO_SPLIT = 512
 CP_MAX_LAYERS = 8
 
 # every symbol include/cp_chain.h declares
@@ -48,11 +49,14 @@ class cp_chain_stats_t(ctypes.Structure):
         ("queue_is_perm", ctypes.c_int32), ("head", ctypes.c_uint32), ("tail", ctypes.c_uint32),
         ("n_queues", ctypes.c_int32), ("queues_drained", ctypes.c_int32),
         ("order_violations", ctypes.c_int32), ("last_run_ms", ctypes.c_double),
-        ("last_kernel_ms", ctypes.c_double),
+        ("last_kernel_ms", ctypes.c_double), ("nonzero_arrivals", ctypes.c_int32),
+        ("nsplit", ctypes.c_int32 * 8),
     ]
 
     def as_dict(self):
-        return {name: getattr(self, name) for name, _ in self._fields_}
+        d = {name: getattr(self, name) for name, _ in self._fields_}
+        d["nsplit"] = list(self.nsplit)
+        return d
 
 
 class CpError(RuntimeError):
