@@ -11,11 +11,14 @@
 // launched without prologue/epilogue for the sequential and micro-batched
 // baselines, so all modes produce bit-identical results.
 //
-// gfx950 mapping (MI355X): 256 threads = 4 wave64 per workgroup; bf16 tiles
-// use v_mfma_f32_32x32x16_bf16 with fp32 accumulators held in AGPRs, fp32
-// tiles use v_mfma_f32_32x32x2_f32.  The paper's system-wide threadfence
-// becomes one agent-scope release per tile (write-back of the XCD-private L2)
-// and the consumer's read of the scoreboard an agent-scope acquire.
+// gfx950 mapping (MI355X): 4 wave64 per workgroup (8 for 256 x 256 tiles);
+// bf16 tiles use v_mfma_f32_32x32x16_bf16 with fp32 accumulators, fp32 tiles
+// v_mfma_f32_32x32x2_f32.  The paper's system-wide threadfence becomes, on
+// one GPU, agent scope: by default the producer writes intermediate tiles
+// with agent-scope (L2 write-through) stores and waits for their completion
+// before it touches a counter; with CP_FLAG_FENCE_RELEASE it is one
+// agent-scope release fence per tile (write-back of the XCD-private L2) and
+// the consumer's read of its counter an agent-scope acquire.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
