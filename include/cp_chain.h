@@ -223,6 +223,18 @@ int cp_chain_tile_graph(int64_t M, int32_t n_layers, const int64_t *widths, int3
                         int32_t tile_n, int32_t *n_tiles, int32_t *n_edges, int32_t *layer_off,
                         int32_t *indeg, int32_t *dep_off, int32_t *dep_ids);
 
+/*
+ * cp_chain_tile_graph_split -- as cp_chain_tile_graph, with nsplit[l] >= 1
+ * work items per tile of layer l (split-K; NULL = no split).  Items of a tile
+ * are consecutive: id = off_l + (i*(N_l/tile_n) + j)*nsplit[l] + s.  Item s
+ * of a consumer tile depends on the producer tiles of its k range only; a
+ * producer tile's out-edges sit on its first item.  Needs nsplit[l] to
+ * divide N_{l-1}/tile_n for l >= 1 and K_0 for l = 0 (CP_ERR_SHAPE).
+ */
+int cp_chain_tile_graph_split(int64_t M, int32_t n_layers, const int64_t *widths, int32_t tile_m,
+                              int32_t tile_n, const int32_t *nsplit, int32_t *n_tiles, int32_t *n_edges,
+                              int32_t *layer_off, int32_t *indeg, int32_t *dep_off, int32_t *dep_ids);
+
 /* static description of a status code */
 const char *cp_chain_error_string(int code);
 /* thread-local detail of the most recent failure on this thread ("" if none) */

@@ -53,8 +53,8 @@ def read_golden(path):
         parts = line.split()
         if parts[0] in ("n_tiles", "n_first", "n_edges"):
             out[parts[0]] = int(parts[1])
-        elif parts[0] == "layer_off":
-            out["layer_off"] = [int(x) for x in parts[1:]]
+        elif parts[0] in ("layer_off", "nsplit", "indeg"):
+            out[parts[0]] = [int(x) for x in parts[1:]]
         else:
             out["edges"][int(parts[0])] = [int(x) for x in parts[1:]]
     return out
@@ -70,6 +70,66 @@ def test_tile_graph_matches_hand_derived_golden():
     for p, cons in gold["edges"].items():
         assert g["dep_ids"][g["dep_off"][p]:g["dep_off"][p + 1]] == cons
     assert g["indeg"] == [0] * 16 + [8] * 16
+
+
+@pytest.mark.parametrize("name, M, widths", [
+    ("split_consumer_tile_graph.txt", 128, [256, 256, 128]),
+    ("split_producer_tile_graph.txt", 64, [256, 128, 64]),
+])
+def test_split_tile_graph_matches_hand_derived_golden(name, M, widths):
+    gold = read_golden(os.path.join(ROOT, "tests", "golden", name))
+    g = nat.cp_chain_tile_graph(M, widths, 64, 64, nsplit=gold["nsplit"])
+    assert g["n_tiles"] == gold["n_tiles"]
+    assert g["n_edges"] == gold["n_edges"]
+    assert g["layer_off"] == gold["layer_off"]
+    assert g["indeg"] == gold["indeg"]
+    for p, cons in gold["edges"].items():
+        assert g["dep_ids"][g["dep_off"][p]:g["dep_off"][p + 1]] == cons, p
+
+
+@pytest.mark.parametrize("M, widths, bn, ns", [
+    (256, [512, 1024, 512, 256], 64, [1, 4, 2]),
+    (128, [1024, 512, 2048], 128, [2, 4]),
+    (384, [256, 768, 384, 768], 64, [4, 2, 3]),
+])
+def test_split_tile_graph_rule(M, widths, bn, ns):
+    """Any split: item s of consumer tile (l+1, i, j) depends on exactly the
+    producer tiles (l, i, k) of its k range, through their first items, and
+    the in-degree equals the number of those tiles."""
+    g = nat.cp_chain_tile_graph(M, widths, 64, bn, nsplit=ns)
+    L, nrb = len(widths) - 1, M // 64
+    nbn = [w // bn for w in widths[1:]]
+    off = [0]
+    for l in range(L):
+        off.append(off[-1] + nrb * nbn[l] * ns[l])
+    assert g["layer_off"] == off
+    item = lambda l, i, j, s: off[l] + (i * nbn[l] + j) * ns[l] + s
+    want = set()
+    for l in range(L - 1):
+        per = nbn[l] // ns[l + 1]
+        for i in range(nrb):
+            for k in range(nbn[l]):
+                for j in range(nbn[l + 1]):
+                    want.add((item(l, i, k, 0), item(l + 1, i, j, k // per)))
+    got = set()
+    for p in range(g["n_tiles"]):
+        for c in g["dep_ids"][g["dep_off"][p]:g["dep_off"][p + 1]]:
+            assert (p, c) not in got
+            got.add((p, c))
+    assert got == want and g["n_edges"] == len(want)
+    indeg = [0] * g["n_tiles"]
+    for _, c in want:
+        indeg[c] += 1
+    assert g["indeg"] == indeg
+
+
+def test_split_tile_graph_rejects_bad_splits():
+    with pytest.raises(nat.CpError) as e:
+        nat.cp_chain_tile_graph(128, [256, 256, 128], 64, 64, nsplit=[1, 3])   # 3 does not divide 4
+    assert e.value.code == nat.CP_ERR_SHAPE
+    with pytest.raises(nat.CpError) as e:
+        nat.cp_chain_tile_graph(128, [256, 256, 128], 64, 64, nsplit=[0, 1])
+    assert e.value.code == nat.CP_ERR_SHAPE
 
 
 def check_graph_rule(M, widths, bm, bn):

@@ -325,12 +325,26 @@ const char *cp_chain_last_error(void) { return g_last_error.c_str(); }
 int cp_chain_tile_graph(int64_t M, int32_t n_layers, const int64_t *widths, int32_t tile_m,
                         int32_t tile_n, int32_t *n_tiles, int32_t *n_edges, int32_t *layer_off,
                         int32_t *indeg, int32_t *dep_off, int32_t *dep_ids) {
+    return cp_chain_tile_graph_split(M, n_layers, widths, tile_m, tile_n, nullptr, n_tiles, n_edges, layer_off,
+                                     indeg, dep_off, dep_ids);
+}
+
+int cp_chain_tile_graph_split(int64_t M, int32_t n_layers, const int64_t *widths, int32_t tile_m,
+                              int32_t tile_n, const int32_t *nsplit, int32_t *n_tiles, int32_t *n_edges,
+                              int32_t *layer_off, int32_t *indeg, int32_t *dep_off, int32_t *dep_ids) {
     g_last_error.clear();
     int rc = check_shape(M, n_layers, widths, tile_m, tile_n, 0);
     if (rc) return rc;
+    if (nsplit)
+        for (int l = 0; l < n_layers; ++l) {
+            const int64_t div = l == 0 ? widths[0] : widths[l] / tile_n;
+            if (nsplit[l] < 1 || div % nsplit[l])
+                return fail(CP_ERR_SHAPE, "nsplit[%d] = %d must be >= 1 and divide %lld", l, nsplit[l],
+                            (long long)div);
+        }
     TileGraph g;
     try {
-        build_graph(M, n_layers, widths, tile_m, tile_n, nullptr, g);
+        build_graph(M, n_layers, widths, tile_m, tile_n, nsplit, g);
     } catch (const std::bad_alloc &) {
         return fail(CP_ERR_OOM, "host allocation failed");
     }

@@ -36,8 +36,8 @@ CP_MAX_LAYERS = 8
 
 # every symbol include/cp_chain.h declares
 EXPORTS = ("cp_chain_plan", "cp_chain_run", "cp_chain_stats", "cp_chain_trace",
-           "cp_chain_destroy", "cp_chain_tile_graph", "cp_chain_error_string",
-           "cp_chain_last_error")
+           "cp_chain_destroy", "cp_chain_tile_graph", "cp_chain_tile_graph_split",
+           "cp_chain_error_string", "cp_chain_last_error")
 
 
 class cp_chain_stats_t(ctypes.Structure):
@@ -99,6 +99,9 @@ _lib.cp_chain_destroy.argtypes = [_vp]
 _lib.cp_chain_tile_graph.restype = ctypes.c_int
 _lib.cp_chain_tile_graph.argtypes = [_i64, _i32, _pi64, _i32, _i32, _pi32, _pi32, _pi32, _pi32,
                                      _pi32, _pi32]
+_lib.cp_chain_tile_graph_split.restype = ctypes.c_int
+_lib.cp_chain_tile_graph_split.argtypes = [_i64, _i32, _pi64, _i32, _i32, _pi32, _pi32, _pi32, _pi32, _pi32,
+                                                _pi32, _pi32]
 _lib.cp_chain_error_string.restype = ctypes.c_char_p
 _lib.cp_chain_error_string.argtypes = [ctypes.c_int]
 _lib.cp_chain_last_error.restype = ctypes.c_char_p
@@ -168,19 +171,28 @@ def cp_chain_destroy(plan):
         _check(_lib.cp_chain_destroy(plan), "cp_chain_destroy")
 
 
-def cp_chain_tile_graph(M, widths, tile_m, tile_n):
+def cp_chain_tile_graph(M, widths, tile_m, tile_n, nsplit=None):
     """Host-only dependency table: dict of n_tiles, n_edges, layer_off, indeg,
-    dep_off, dep_ids (python lists)."""
+    dep_off, dep_ids (python lists).  nsplit: split-K items per tile of each
+    layer (cp_chain_tile_graph_split), or None."""
     L = len(widths) - 1
     w = _i64_array(widths)
     T, E = ctypes.c_int32(), ctypes.c_int32()
-    _check(_lib.cp_chain_tile_graph(int(M), L, w, int(tile_m), int(tile_n), ctypes.byref(T),
-                                    ctypes.byref(E), None, None, None, None), "cp_chain_tile_graph")
+    if nsplit is None:
+        def call(*outs):
+            return _lib.cp_chain_tile_graph(int(M), L, w, int(tile_m), int(tile_n), *outs)
+        where = "cp_chain_tile_graph"
+    else:
+        ns = (ctypes.c_int32 * L)(*[int(x) for x in nsplit])
+
+        def call(*outs):
+            return _lib.cp_chain_tile_graph_split(int(M), L, w, int(tile_m), int(tile_n), ns, *outs)
+        where = "cp_chain_tile_graph_split"
+    _check(call(ctypes.byref(T), ctypes.byref(E), None, None, None, None), where)
     off = (ctypes.c_int32 * (L + 1))()
     indeg = (ctypes.c_int32 * max(T.value, 1))()
     doff = (ctypes.c_int32 * (T.value + 1))()
     dids = (ctypes.c_int32 * max(E.value, 1))()
-    _check(_lib.cp_chain_tile_graph(int(M), L, w, int(tile_m), int(tile_n), ctypes.byref(T),
-                                    ctypes.byref(E), off, indeg, doff, dids), "cp_chain_tile_graph")
+    _check(call(ctypes.byref(T), ctypes.byref(E), off, indeg, doff, dids), where)
     return {"n_tiles": T.value, "n_edges": E.value, "layer_off": list(off),
             "indeg": list(indeg)[:T.value], "dep_off": list(doff), "dep_ids": list(dids)[:E.value]}
