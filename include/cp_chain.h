@@ -89,12 +89,15 @@ typedef struct cp_chain cp_chain; /* opaque plan */
  * relies on the device being otherwise idle (else the watchdog may end the
  * run with CP_ERR_TIMEOUT) */
 #define CP_FLAG_COOPERATIVE 64u
-/* pipelined mode: release every producer tile with an agent-scope fence
- * (write-back of its XCD's whole L2) and acquire every consumer tile with an
- * L2 invalidate, the plain memory-model protocol.  Default: intermediates are
- * stored at agent scope (write-through), each producer waits until its stores
- * have completed before it decrements a counter, and consumers need no
- * invalidate */
+/* release protocol of the pipelined and spatial modes (both exact):
+ *   write-through (default): intermediates are stored at agent scope
+ *     (write-through of the XCD's L2), each producer waits until its stores
+ *     have completed before it decrements a counter, and consumers need no
+ *     invalidate;
+ *   CP_FLAG_FENCE_RELEASE: every producer tile is released with an
+ *     agent-scope fence (write-back of its XCD's whole L2) and every consumer
+ *     tile acquired with an L2 invalidate, the plain memory-model protocol.
+ * cp_chain_stats reports the protocol in use. */
 #define CP_FLAG_FENCE_RELEASE 128u
 /* record HIP timing events around every run (cp_chain_stats then reports
  * last_run_ms / last_kernel_ms); each event stalls the stream for a few
@@ -128,6 +131,7 @@ typedef struct cp_chain_stats_t {
                                 (poison fills excluded); otherwise same as last_run_ms    */
     int32_t nonzero_arrivals;/* split-K tiles whose arrival count did not end at 0        */
     int32_t nsplit[CP_MAX_LAYERS]; /* split-K items per tile of each layer (1 = no split) */
+    int32_t fenced;          /* release protocol of the plan: 1 fence, 0 write-through   */
 } cp_chain_stats_t;
 
 /*

@@ -146,7 +146,8 @@ def test_signed_permutation_chain_exact_with_poison(rt, dtype, release):
     that read an intermediate before its producers published would show.
     Both release protocols (write-through stores, or a fence per tile)."""
     f = rt_flags()
-    extra = rt["nat"].CP_FLAG_FENCE_RELEASE if release == "fence" else 0
+    nat = rt["nat"]
+    extra = nat.CP_FLAG_FENCE_RELEASE if release == "fence" else 0
     tile = (64, 64) if dtype == gen.F32 else (128, 128)
     n = 512 if dtype == gen.F32 else 1024
     M = 4 * tile[0]
@@ -155,6 +156,7 @@ def test_signed_permutation_chain_exact_with_poison(rt, dtype, release):
     say("perm chain", dtype, tile, M, n, release)
     out, st = run_modes(rt, X, Ws, dtype, tile, flags=all_flags() | f["DELAY"] | extra,
                         modes=("pipelined", "sequential", "spatial"), reps=3)
+    assert st["fenced"] == (1 if release == "fence" else 0), st
     ref = oracle.chain(X, Ws, dtype)
     assert np.array_equal(as_values(out["pipelined"], dtype), ref)
     assert np.array_equal(as_values(out["sequential"], dtype), ref)
@@ -204,8 +206,9 @@ def test_many_tiles_many_waves(rt):
     M, widths = 4096, (256, 1024, 320)   # 64 row-blocks of 64: 1024 + 320 tiles
     X, Ws = gen.chain_inputs(M, widths, gen.BF16, 1.0, (1 / 16, 1 / 32), 81)
     out, st = run_modes(rt, X, Ws, gen.BF16, (64, 64), flags=all_flags(), reps=2)
-    say("workers", st["n_workers"], "tiles", st["n_tiles"])
+    say("workers", st["n_workers"], "tiles", st["n_tiles"], "fenced", st["fenced"])
     assert st["n_tiles"] > st["n_workers"]
+    assert st["fenced"] == 0
     ref = oracle.chain(X, Ws, gen.BF16)
     assert oracle.rel_err(as_values(out["pipelined"], gen.BF16), ref) <= TOL[gen.BF16]
     assert same_bits(out["pipelined"], out["sequential"])

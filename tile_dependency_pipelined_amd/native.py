@@ -50,7 +50,7 @@ class cp_chain_stats_t(ctypes.Structure):
         ("n_queues", ctypes.c_int32), ("queues_drained", ctypes.c_int32),
         ("order_violations", ctypes.c_int32), ("last_run_ms", ctypes.c_double),
         ("last_kernel_ms", ctypes.c_double), ("nonzero_arrivals", ctypes.c_int32),
-        ("nsplit", ctypes.c_int32 * 8),
+        ("nsplit", ctypes.c_int32 * 8), ("fenced", ctypes.c_int32),
     ]
 
     def as_dict(self):
