@@ -38,7 +38,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="c3")
     ap.add_argument("--tile", default=None, help="override tile, e.g. 256x128")
     ap.add_argument("--reps", type=int, default=20, help="reps per mode for the baseline comparison")
@@ -191,47 +191,50 @@ def main():
 
 
 def compare_modes(plan, step, stream, cfg, tile, reps, torch, tuning):
-    """Median event-timed latency of each mode, warm (back to back) and cold
-    (a 1 GiB device write between reps, outside the timed span)."""
+    """Latency of single runs of each mode, warm (back to back) and cold (a
+    1 GiB device write before each run, outside the timed span).  The modes
+    are interleaved, one run of each per round, so that clock and thermal
+    drift affect them alike; a short GPU sleep before the start event keeps
+    host submission time out of the span.  Median, min, p10, p90 per mode."""
     scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    runs = [("pipelined", 0), ("sequential", 0), ("spatial", 0)]
+    runs += [("microbatch", m) for m in tuning.chunk_sweep(cfg.M, tile[0])]
 
-    def timed(mode, mb, cold):
-        ts = []
-        for _ in range(3):
-            step(mode, mb)
-        for _ in range(reps):
-            if cold:
-                scrub.fill_(1.0)
-            # keep the GPU busy while the host submits the run, so that the
-            # start event is not timestamped before the run can begin
-            torch.cuda._sleep(200000)
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            step(mode, mb)
-            e1.record(stream)
-            e1.synchronize()
-            ts.append(e0.elapsed_time(e1) * 1e3)
-        ts.sort()
+    def one(mode, mb, cold):
+        if cold:
+            scrub.fill_(1.0)
+        torch.cuda._sleep(200000)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step(mode, mb)
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e3
+
+    def summary(ts):
+        ts = sorted(ts)
         return {"median_us": round(statistics.median(ts), 1), "min_us": round(ts[0], 1),
                 "p10_us": round(ts[len(ts) // 10], 1), "p90_us": round(ts[(9 * len(ts)) // 10], 1)}
 
     out = {}
+    for mode, mb in runs:
+        for _ in range(3):
+            step(mode, mb)
     for cold in (False, True):
         tag = "cold" if cold else "warm"
-        out[f"pipelined_{tag}"] = timed("pipelined", 0, cold)
-        out[f"sequential_{tag}"] = timed("sequential", 0, cold)
-        out[f"spatial_{tag}"] = timed("spatial", 0, cold)
-        best = None
-        sweep = {}
-        for m in tuning.chunk_sweep(cfg.M, tile[0]):
-            r = timed("microbatch", m, cold)
-            sweep[str(m)] = r["median_us"]
-            if best is None or r["median_us"] < best[1]["median_us"]:
-                best = (m, r)
-        if best:
-            out[f"microbatch_best_{tag}"] = dict(best[1], chunk_rows=best[0])
-            out[f"microbatch_sweep_{tag}"] = sweep
+        ts = {r: [] for r in runs}
+        for _ in range(reps):
+            for r in runs:
+                ts[r].append(one(r[0], r[1], cold))
+        for name in ("pipelined", "sequential", "spatial"):
+            out[f"{name}_{tag}"] = summary(ts[(name, 0)])
+        mbs = [r for r in runs if r[0] == "microbatch"]
+        if mbs:
+            sw = {str(r[1]): summary(ts[r]) for r in mbs}
+            best = min(mbs, key=lambda r: sw[str(r[1])]["median_us"])
+            out[f"microbatch_best_{tag}"] = dict(sw[str(best[1])], chunk_rows=best[1])
+            out[f"microbatch_sweep_{tag}"] = {k: v["median_us"] for k, v in sw.items()}
         log(tag, {k: v for k, v in out.items() if k.endswith(tag)})
     del scrub
     return out
