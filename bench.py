@@ -246,9 +246,12 @@ def cpu_baseline(cfg, X, Ws, rows):
     import numpy as np
     import oracle
     if rows <= 0:
-        # about 10 s of CPU work at ~1 GFLOP/s per thread
-        per_row = cfg.flops / cfg.M
-        rows = int(max(1, min(cfg.M, 10e9 * oracle.num_threads() / per_row)))
+        # about 10 s of CPU work: rate from a short calibration sample
+        probe = min(cfg.M, 16)
+        t0 = time.perf_counter()
+        oracle.chain(X, Ws, cfg.dtype, acts=list(cfg.acts), rows=np.arange(probe, dtype=np.int64))
+        per_row_s = (time.perf_counter() - t0) / probe
+        rows = int(max(1, min(cfg.M, 10.0 / per_row_s)))
     sel = np.arange(rows, dtype=np.int64)
     t0 = time.perf_counter()
     oracle.chain(X, Ws, cfg.dtype, acts=list(cfg.acts), rows=sel)
