@@ -355,13 +355,16 @@ def test_full_size_sampled_parity(rt, key):
     say(key, "generating inputs")
     X, Ws = gen.config_inputs(cfg)
     say(key, "running tile", tile)
+    chunks = tuning.chunk_sweep(cfg.M, tile[0])
+    mb = chunks[len(chunks) // 2] if chunks else tile[0]
     out, st = run_modes(rt, X, Ws, cfg.dtype, tile, acts=list(cfg.acts), flags=rt_flags()["DEBUG"],
-                        modes=("pipelined", "sequential"))
+                        modes=("pipelined", "sequential", "spatial", "microbatch"), mb_rows=mb)
     rows = sample_rows(cfg.M, tile[0])
     say(key, "oracle rows", rows.tolist())
     ref = oracle.chain(X, Ws, cfg.dtype, acts=list(cfg.acts), rows=rows)
     err = oracle.rel_err(as_values(out["pipelined"][rows], cfg.dtype), ref)
     say(key, "sampled rel err", err, "stats", st)
     assert err <= TOL[gen.BF16]
-    assert same_bits(out["pipelined"], out["sequential"])
+    for mode in ("sequential", "spatial", "microbatch"):
+        assert same_bits(out["pipelined"], out[mode]), mode
     assert np.all(np.isfinite(as_values(out["pipelined"], cfg.dtype)))
