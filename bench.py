@@ -183,6 +183,9 @@ def main():
     if not args.no_modes and not args.profile:
         result["modes"] = compare_modes(plan, step, stream, cfg, tile, args.reps, torch, tuning)
 
+    if not args.profile and cfg.dtype == gen.BF16:
+        result["clock"] = clock_breakdown(cfg, tile, step, torch, ch, nat)
+
     if not args.no_cpu_baseline and not args.profile:
         result["cpu_baseline"] = cpu_baseline(cfg, X, Ws, args.cpu_sample_rows)
 
@@ -237,6 +240,52 @@ def compare_modes(plan, step, stream, cfg, tile, reps, torch, tuning):
             out[f"microbatch_sweep_{tag}"] = {k: v["median_us"] for k, v in sw.items()}
         log(tag, {k: v for k, v in out.items() if k.endswith(tag)})
     del scrub
+    return out
+
+
+def clock_breakdown(cfg, tile, step, torch, ch, nat, runs=5):
+    """Shader clock and MFMA cycle efficiency of the tile bodies, from the
+    per-tile trace (CP_FLAG_TRACE) of a few back-to-back pipelined runs: a
+    tile's clock is its shader-clock cycles over its wall-clock span, its
+    MFMA cycle fraction the cycles a compute unit needs at the bf16 MFMA
+    rate (4 SIMDs x 1024 flop per cycle) over the cycles it took.  Grouped
+    by queue, i.e. by XCD: under the power cap the XCDs run at different
+    clocks, and the slowest one sets when a layer's row-blocks complete."""
+    import numpy as np
+    L = len(cfg.widths) - 1
+    with ch.Chain(cfg.M, cfg.widths, cfg.dtype, tile[0], tile[1], acts=list(cfg.acts),
+                  flags=nat.CP_FLAG_TRACE) as pt:
+        st = pt.stats()
+        nsplit = st["nsplit"][:L]
+        nq = st["n_queues"]
+        for _ in range(10):
+            step(p=pt)
+        ghz, frac, queue = [], [], []
+        for _ in range(runs):
+            step(p=pt)
+            pt.stats()
+            tr = np.array(pt.trace(), dtype=np.uint64).reshape(-1, nat.CP_TRACE_WORDS).astype(np.int64)
+            off = 0
+            for l in range(L):
+                nbn = cfg.widths[l + 1] // tile[1]
+                n = (cfg.M // tile[0]) * nbn * nsplit[l]
+                s = tr[off:off + n]
+                off += n
+                wall = s[:, 2] - s[:, 1]
+                cyc = s[:, 5] - s[:, 4]
+                ideal = 2.0 * tile[0] * tile[1] * (cfg.widths[l] / nsplit[l]) / 4096.0
+                j = (np.arange(n) // nsplit[l]) % nbn
+                ghz.append(cyc / wall * 0.1)
+                frac.append(ideal / cyc)
+                queue.append(j % nq)
+    ghz, frac, queue = np.concatenate(ghz), np.concatenate(frac), np.concatenate(queue)
+    by_q = [round(float(np.median(ghz[queue == q])), 3) for q in range(nq)]
+    med = float(np.median(ghz))
+    out = {"shader_ghz_median": round(med, 3), "shader_ghz_by_queue": by_q,
+           "mfma_cycle_frac_median": round(float(np.median(frac)), 3),
+           "bf16_peak_at_median_clock_tflops": round(256 * 4096 * med * 1e9 / 1e12, 1),
+           "runs": runs, "source": "CP_FLAG_TRACE shader-clock and wall-clock stamps per tile"}
+    log("clock", out)
     return out
 
 

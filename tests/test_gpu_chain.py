@@ -214,6 +214,33 @@ def test_many_tiles_many_waves(rt):
     assert same_bits(out["pipelined"], out["sequential"])
 
 
+def test_trace_stamps(rt):
+    """The trace holds, per tile, wall-clock stamps in protocol order (ticket
+    taken <= dequeued <= body done <= released) and shader-clock stamps
+    whose ratio to the wall clock is a plausible clock frequency."""
+    torch, ch, nat = rt["torch"], rt["chain"], rt["nat"]
+    M, widths = 512, (512, 1024, 512)
+    X, Ws = gen.chain_inputs(M, widths, gen.BF16, 1.0, (1 / np.sqrt(512), 1 / 32), 85)
+    dX = ch.to_device(X, gen.BF16)
+    dW = [ch.to_device(w, gen.BF16) for w in Ws]
+    dY = torch.empty((M, widths[-1]), dtype=torch.bfloat16, device="cuda")
+    with ch.Chain(M, widths, gen.BF16, 128, 128, flags=nat.CP_FLAG_TRACE) as c:
+        c.run(dX, dW, dY)
+        st = c.stats()
+        check_invariants(st, nat.CP_FLAG_TRACE)
+        tr = np.array(c.trace(), dtype=np.uint64).reshape(-1, nat.CP_TRACE_WORDS).astype(np.int64)
+    T = st["n_tiles"]
+    first_layer = (M // 128) * (widths[1] // 128)
+    assert tr.shape == (T, 6)
+    assert (tr[:, 0] <= tr[:, 1]).all() and (tr[:, 1] < tr[:, 2]).all()
+    assert (tr[:first_layer, 3] >= tr[:first_layer, 2]).all()   # producers released after their body
+    assert (tr[first_layer:, 3] == 0).all()                       # last layer releases nothing
+    cycles = tr[:, 5] - tr[:, 4]
+    ghz = cycles / (tr[:, 2] - tr[:, 1]) * 0.1
+    say("trace: shader clock GHz min %.2f median %.2f max %.2f" % (ghz.min(), np.median(ghz), ghz.max()))
+    assert (cycles > 0).all() and 0.3 < np.median(ghz) < 3.0
+
+
 @pytest.mark.parametrize("coop", [False, True], ids=["plain", "cooperative"])
 def test_pipelined_repeats_alternate_state(rt, coop):
     """Back-to-back pipelined runs alternate between the plan's two copies of

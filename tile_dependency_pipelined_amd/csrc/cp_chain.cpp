@@ -433,7 +433,7 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
         o_score[c] = off; off = align_up(off + T * 4, 256);
         o_queue[c] = off; off = align_up(off + T * 4, 256);
         o_deq[c] = off;   off = align_up(off + T * 4, 256);
-        o_trace[c] = off; off = align_up(off + ((flags & CP_FLAG_TRACE) ? T * 32 : 0), 256);
+        o_trace[c] = off; off = align_up(off + ((flags & CP_FLAG_TRACE) ? T * 8 * cp::kTraceWords : 0), 256);
     }
     const size_t o_indeg = off;   off = align_up(off + T * 4, 256);
     const size_t o_doff = off;    off = align_up(off + (T + 1) * 4, 256);
@@ -834,13 +834,13 @@ int cp_chain_stats(cp_chain *p, cp_chain_stats_t *out) {
         out->bad_dequeues = bad;
     }
     if (p->flags & CP_FLAG_TRACE) {
-        std::vector<uint64_t> tr(T * 4);
-        CP_HIP(hipMemcpy(tr.data(), p->d_trace[c], T * 32, hipMemcpyDeviceToHost));
+        std::vector<uint64_t> tr(T * cp::kTraceWords);
+        CP_HIP(hipMemcpy(tr.data(), p->d_trace[c], T * 8 * cp::kTraceWords, hipMemcpyDeviceToHost));
         int32_t viol = 0;
         for (size_t pr = 0; pr < T; ++pr)
             for (int32_t e = p->g.dep_off[pr]; e < p->g.dep_off[pr + 1]; ++e) {
                 const size_t c = (size_t)p->g.dep_ids[e];
-                if (tr[4 * c + 1] < tr[4 * pr + 3]) ++viol;  // consumer dequeued before producer released
+                if (tr[cp::kTraceWords * c + 1] < tr[cp::kTraceWords * pr + 3]) ++viol;  // consumer dequeued before producer released
             }
         out->order_violations = viol;
     }
@@ -852,10 +852,11 @@ int cp_chain_trace(cp_chain *p, uint64_t *out, int64_t capacity) {
     g_last_error.clear();
     if (!p || !out) return fail(CP_ERR_INVALID_ARG, "plan or out is NULL");
     if (!(p->flags & CP_FLAG_TRACE)) return fail(CP_ERR_INVALID_ARG, "plan was built without CP_FLAG_TRACE");
-    if (capacity < 4 * (int64_t)p->g.T) return fail(CP_ERR_INVALID_ARG, "capacity %lld < 4*T", (long long)capacity);
+    if (capacity < cp::kTraceWords * (int64_t)p->g.T)
+        return fail(CP_ERR_INVALID_ARG, "capacity %lld < %d*T", (long long)capacity, cp::kTraceWords);
     int rc = wait_last(p);
     if (rc) return rc;
-    CP_HIP(hipMemcpy(out, p->d_trace[p->last_copy], (size_t)p->g.T * 32, hipMemcpyDeviceToHost));
+    CP_HIP(hipMemcpy(out, p->d_trace[p->last_copy], (size_t)p->g.T * 8 * cp::kTraceWords, hipMemcpyDeviceToHost));
     return CP_OK;
 }
 

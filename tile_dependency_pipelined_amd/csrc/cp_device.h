@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "cp_chain.h"
+
 namespace cp {
 
 constexpr int kMaxLayers = 8;
@@ -16,6 +18,9 @@ constexpr uint32_t kDone = 0xFFFFFFFEu;    // prologue: no more work
 // so there is one queue per XCD.  A tile belongs to the queue of its column
 // panel (j mod nq): the weight panel it reads then stays in one XCD's L2.
 constexpr int kMaxQueues = 8;
+// trace words per tile: ticket taken, dequeued, body done, released (100 MHz
+// wall clock), then the shader clock counter at dequeue and at body done
+constexpr int kTraceWords = CP_TRACE_WORDS;
 
 // Control words, each on its own 128-byte line: per queue a ticket counter
 // (head) and a push counter (tail), then the run status.
@@ -66,7 +71,7 @@ struct ChainArgs {
     const int32_t *indeg;    // [T] initial scoreboard (reset source)
     const uint32_t *qinit;   // [T] initial queue contents (reset source)
     uint32_t *deq_count;     // [T] debug: dequeues per tile, or null
-    uint64_t *trace;         // [4T] timestamps, or null
+    uint64_t *trace;         // [kTraceWords T] timestamps, or null
     uint32_t *arrive;        // [T] split-K: items of a tile that finished (at its first item's
                              // index); the last one sums the partials and resets it to 0
     // the other copy of the per-run state (queue, ctl, score, deq_count,

@@ -682,8 +682,9 @@ __device__ uint32_t wait_slot(const ChainArgs &a, int q, uint32_t t) {
     if (a.deq_count)
         __hip_atomic_fetch_add(a.deq_count + id, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (a.trace) {
-        a.trace[4 * (size_t)id + 0] = t0;
-        a.trace[4 * (size_t)id + 1] = wall_clock64();
+        a.trace[kTraceWords * (size_t)id + 0] = t0;
+        a.trace[kTraceWords * (size_t)id + 1] = wall_clock64();
+        a.trace[kTraceWords * (size_t)id + 4] = clock64();
     }
     return id;
 }
@@ -711,7 +712,7 @@ __device__ void publish(const ChainArgs &a, uint32_t id, int l) {
         const uint64_t s = wall_clock64();
         while (wall_clock64() - s < 2000) __builtin_amdgcn_s_sleep(8);  // ~20 us
     }
-    if (a.trace && lane == 0) a.trace[4 * (size_t)id + 3] = wall_clock64();
+    if (a.trace && lane == 0) a.trace[kTraceWords * (size_t)id + 3] = wall_clock64();
     const LayerDesc &next = a.layer[l + 1];
     const int beg = a.dep_off[id], end = a.dep_off[id + 1];
     for (int e0 = beg; e0 < end; e0 += 64) {
@@ -776,12 +777,8 @@ __device__ void reset_copy(const ChainArgs &a, uint32_t *queue, uint32_t *ctl, i
         queue[t] = a.qinit[t];
         arrive[t] = 0;
         if (deq_count) deq_count[t] = 0;
-        if (trace) {
-            trace[4 * (size_t)t + 0] = 0;
-            trace[4 * (size_t)t + 1] = 0;
-            trace[4 * (size_t)t + 2] = 0;
-            trace[4 * (size_t)t + 3] = 0;
-        }
+        if (trace)
+            for (int w = 0; w < kTraceWords; ++w) trace[kTraceWords * (size_t)t + w] = 0;
     }
     if (blockIdx.x == 0 && threadIdx.x < kMaxQueues) {
         const int q = threadIdx.x;
@@ -830,7 +827,10 @@ __global__ void __launch_bounds__(Body::NT) worker_kernel(ChainArgs a) {
         const bool done = Body::template run<SPLIT>(a.layer[l], i, j, split, a.arrive + first, stg, [&] {
             if (sched) ticket = take_ticket(a, q);
         });
-        if (a.trace && threadIdx.x == 0) a.trace[4 * (size_t)id + 2] = wall_clock64();
+        if (a.trace && threadIdx.x == 0) {
+            a.trace[kTraceWords * (size_t)id + 2] = wall_clock64();
+            a.trace[kTraceWords * (size_t)id + 5] = clock64();
+        }
         // after publish's opening barrier wave 0 releases the tile while the
         // scheduler lane (wave 1) already waits for the next one; a split-K
         // item that did not complete its tile has nothing to release

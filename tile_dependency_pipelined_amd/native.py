@@ -160,9 +160,12 @@ def cp_chain_stats(plan, check=True):
     return d
 
 
+CP_TRACE_WORDS = 6
+
+
 def cp_chain_trace(plan, n_tiles):
-    buf = (ctypes.c_uint64 * (4 * n_tiles))()
-    _check(_lib.cp_chain_trace(plan, buf, 4 * n_tiles), "cp_chain_trace")
+    buf = (ctypes.c_uint64 * (CP_TRACE_WORDS * n_tiles))()
+    _check(_lib.cp_chain_trace(plan, buf, CP_TRACE_WORDS * n_tiles), "cp_chain_trace")
     return list(buf)
 
 

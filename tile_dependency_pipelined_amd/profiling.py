@@ -5,6 +5,7 @@ back the HBM traffic figure the benchmark reports.
     python -m tile_dependency_pipelined_amd.profiling summarize \
         --workload c3 --tile 256x256 --stats <kernel_stats.csv> \
         --fetch <counter_collection.csv> --write <counter_collection.csv> \
+        [--pmc <counter_collection.csv> ...] \
         --cmd "<the commands that made the inputs>" --out profiles/<name>.md
 
 Traffic: FETCH_SIZE and WRITE_SIZE (KiB per dispatch, from two separate
@@ -147,6 +148,13 @@ def summarize(args):
         kv[f"{tag}_copy_kib_raw"] = f"{c_kib:.0f}"
         kv[f"{tag}_scale"] = f"{scale:.4f}"
         kv[f"{tag}_bytes_per_launch"] = f"{w_kib * 1024 * scale:.0f}"
+    for path in args.pmc:
+        rows = read_csv(path)
+        names = sorted({_get(r, "Counter_Name", "Counter-Name") for r in rows} - {None})
+        for counter in names:
+            wk = counter_per_dispatch(rows, lambda n: WORKER in n, counter)
+            if wk:
+                kv[f"pmc_{counter}_per_launch"] = f"{statistics.median(wk.values()):.6g}"
     if "fetch_bytes_per_launch" in kv and "write_bytes_per_launch" in kv:
         kv["hbm_bytes_per_launch"] = str(int(float(kv["fetch_bytes_per_launch"]) +
                                              float(kv["write_bytes_per_launch"])))
@@ -169,6 +177,9 @@ def main(argv=None):
     s.add_argument("--stats")
     s.add_argument("--fetch")
     s.add_argument("--write")
+    s.add_argument("--pmc", action="append", default=[],
+                   help="further counter_collection.csv files; the worker kernel's median per "
+                        "dispatch of every counter in them is recorded")
     s.add_argument("--cmd", action="append", default=[])
     s.add_argument("--out", required=True)
     args = ap.parse_args(argv)
