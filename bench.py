@@ -183,6 +183,8 @@ def main():
     if not args.no_modes and not args.profile:
         result["modes"] = compare_modes(plan, step, stream, cfg, tile, args.reps, torch, tuning)
 
+    if not args.profile:
+        result["gpu_state_after_timed_steps"] = gpu_state()
     if not args.profile and cfg.dtype == gen.BF16:
         result["clock"] = clock_breakdown(cfg, tile, step, torch, ch, nat)
 
@@ -241,6 +243,21 @@ def compare_modes(plan, step, stream, cfg, tile, reps, torch, tuning):
         log(tag, {k: v for k, v in out.items() if k.endswith(tag)})
     del scrub
     return out
+
+
+def gpu_state():
+    """Power cap, power draw, clocks and temperature as rocm-smi reports them
+    (its JSON, card 0), or the reason they are missing."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showmaxpower", "--showpower", "--showclocks", "--showtemp",
+                            "--showperflevel", "--json"], capture_output=True, text=True, timeout=30)
+        d = json.loads(r.stdout)
+        card = d.get("card0") or next(iter(d.values()))
+        keep = ("power", "clock", "temperature", "performance level", "sclk", "mclk", "fclk")
+        return {k: v for k, v in card.items() if any(w in k.lower() for w in keep)}
+    except Exception as e:  # rocm-smi absent or its output not JSON: report, do not fail the bench
+        return {"error": f"{type(e).__name__}: {e}"[:200]}
 
 
 def clock_breakdown(cfg, tile, step, torch, ch, nat, runs=5):

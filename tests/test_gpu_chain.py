@@ -308,6 +308,23 @@ def test_split_k_layers(rt, acts):
     assert oracle.rel_err(as_values(out2["pipelined"], gen.BF16), ref) <= TOL[gen.BF16]
 
 
+def test_split_k_many_partials(rt):
+    """A long-k layer with two tiles is split into 16 items per tile, so the
+    last item to arrive sums its partials in several groups of loads; the
+    sum keeps split order, so every mode gives the same bits."""
+    M, widths = 128, (16384, 256, 256)
+    X, Ws = gen.chain_inputs(M, widths, gen.BF16, 1.0, (1 / 128, 1 / 16), 87)
+    say("split-K chain with many partials", M, widths)
+    out, st = run_modes(rt, X, Ws, gen.BF16, (128, 128), acts=[gen.ACT_GELU_TANH, gen.ACT_NONE],
+                        flags=all_flags(), modes=("pipelined", "sequential", "microbatch"), mb_rows=128, reps=2)
+    say("nsplit", st["nsplit"], "items", st["n_tiles"])
+    assert st["nsplit"][0] >= 8, st["nsplit"]
+    ref = oracle.chain(X, Ws, gen.BF16, acts=[gen.ACT_GELU_TANH, gen.ACT_NONE])
+    assert oracle.rel_err(as_values(out["pipelined"], gen.BF16), ref) <= TOL[gen.BF16]
+    for m in ("sequential", "microbatch"):
+        assert same_bits(out["pipelined"], out[m]), m
+
+
 def test_rejects_bad_shapes_on_device(rt):
     nat = rt["nat"]
     with pytest.raises(nat.CpError) as e:

@@ -375,38 +375,48 @@ struct Bf16Body {
             const bool last = *word == (uint32_t)(dp->nsplit - 1);
             __syncthreads();  // everyone has read the word before the LDS is reused
             if (!last) return false;
-            // Last to arrive: every other item's partial is in memory.  Reset
-            // the count for the next run and sum the partials in split order
-            // (the same order whichever item arrives last), reading them at
-            // agent scope so that no cached line can be stale.
+            // Last to arrive: every item's partial, this one's included, is in
+            // memory.  Reset the count for the next run and sum the partials in
+            // split order (the same order whichever item arrives last), reading
+            // them at agent scope so that no cached line can be stale.  The
+            // loads of up to four partials of one 32x32 block are all issued
+            // before any of them is used: one memory round trip per block and
+            // group of four, instead of one per partial and 8-byte pair.
             if (tid == 0) __hip_atomic_store(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             const float *ws0 = dp->ws + (size_t)(tile * dp->nsplit) * (BM * BN);
+            const int ns = dp->nsplit;
+            constexpr int G = 4;                   // partials loaded per group
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-                for (int fn = 0; fn < FN; ++fn)
+                for (int fn = 0; fn < FN; ++fn) {
+                    const size_t o = ((((size_t)wave * FM + fm) * FN + fn) * 8) * 128 + lane * 2;
+                    f32x16_t sum;
+                    for (int k0 = 0; k0 < ns; k0 += G) {
+                        uint64_t v[G][8];
 #pragma unroll
-                    for (int h = 0; h < 8; ++h) {
-                        const size_t o = ((((size_t)wave * FM + fm) * FN + fn) * 8 + h) * 128 + lane * 2;
-                        float s0 = 0.0f, s1 = 0.0f;
-                        for (int k = 0; k < dp->nsplit; ++k) {
-                            float v0, v1;
-                            if (k == split) {
-                                v0 = acc[fm][fn][2 * h];
-                                v1 = acc[fm][fn][2 * h + 1];
-                            } else {
-                                const uint64_t v = __hip_atomic_load(
-                                    reinterpret_cast<const uint64_t *>(ws0 + (size_t)k * (BM * BN) + o),
+                        for (int g = 0; g < G; ++g) {
+                            const int k = k0 + g < ns ? k0 + g : ns - 1;  // in range; unused past ns
+#pragma unroll
+                            for (int h = 0; h < 8; ++h)
+                                v[g][h] = __hip_atomic_load(
+                                    reinterpret_cast<const uint64_t *>(ws0 + (size_t)k * (BM * BN) + o + h * 128),
                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                                v0 = __uint_as_float((uint32_t)v);
-                                v1 = __uint_as_float((uint32_t)(v >> 32));
-                            }
-                            s0 = k == 0 ? v0 : s0 + v0;
-                            s1 = k == 0 ? v1 : s1 + v1;
                         }
-                        acc[fm][fn][2 * h] = s0;
-                        acc[fm][fn][2 * h + 1] = s1;
+#pragma unroll
+                        for (int g = 0; g < G; ++g) {
+                            if (k0 + g >= ns) break;
+#pragma unroll
+                            for (int h = 0; h < 8; ++h) {
+                                const float v0 = __uint_as_float((uint32_t)v[g][h]);
+                                const float v1 = __uint_as_float((uint32_t)(v[g][h] >> 32));
+                                sum[2 * h] = k0 + g == 0 ? v0 : sum[2 * h] + v0;
+                                sum[2 * h + 1] = k0 + g == 0 ? v1 : sum[2 * h + 1] + v1;
+                            }
+                        }
                     }
+                    acc[fm][fn] = sum;
+                }
         }
 
         // Epilogue: activation on the fp32 accumulator, RNE to bf16, then the
