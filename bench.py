@@ -167,10 +167,17 @@ def main():
         del a, b
 
     traffic = traffic_from_profile(cfg.key, tile)
-    bound = "mfma"
+    # the roofline that bounds the chain: MFMA above the ridge point (peak
+    # flop/s over peak HBM bytes/s), HBM below it (C5: 254 flop/B < 312.5)
+    intensity = flops / cfg.min_bytes()
+    if intensity >= peak * 1e12 / (PEAK_HBM_GBS * 1e9):
+        bound, achieved, peak_b, unit = "mfma", kernel_tflops, peak, "TFLOP/s"
+    else:
+        bound, achieved, peak_b, unit = "hbm", cfg.min_bytes() / (kernel_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
     result["roofline"] = {
-        "bound": bound, "achieved": round(kernel_tflops, 2), "peak": peak, "unit": "TFLOP/s",
-        "frac": round(kernel_tflops / peak, 4),
+        "bound": bound, "achieved": round(achieved, 2), "peak": peak_b, "unit": unit,
+        "frac": round(achieved / peak_b, 4), "tflops": round(kernel_tflops, 2),
+        "arithmetic_intensity_flop_per_byte": round(intensity, 1),
         "traffic": traffic,
         "kernel": "cp::worker_kernel<Bf16Body<%d,%d,...>>" % tile if cfg.dtype == gen.BF16 else "worker_kernel<F32Body>",
         "kernel_us": round(kernel_ms * 1e3, 1),
