@@ -272,7 +272,8 @@ def clock_breakdown(cfg, tile, step, torch, ch, nat, runs=5):
     per-tile trace (CP_FLAG_TRACE) of a few back-to-back pipelined runs: a
     tile's clock is its shader-clock cycles over its wall-clock span, its
     MFMA cycle fraction the cycles a compute unit needs at the bf16 MFMA
-    rate (4 SIMDs x 1024 flop per cycle) over the cycles it took.  Grouped
+    rate (4 SIMDs x 1024 flop per cycle), times the workgroups that share a
+    compute unit (a tile has that fraction of it), over the cycles it took.  Grouped
     by queue, i.e. by XCD: under the power cap the XCDs run at different
     clocks, and the slowest one sets when a layer's row-blocks complete."""
     import numpy as np
@@ -281,6 +282,7 @@ def clock_breakdown(cfg, tile, step, torch, ch, nat, runs=5):
                   flags=nat.CP_FLAG_TRACE) as pt:
         st = pt.stats()
         nsplit = st["nsplit"][:L]
+        per_cu = st["n_workers"] / torch.cuda.get_device_properties(0).multi_processor_count
         nq = st["n_queues"]
         for _ in range(10):
             step(p=pt)
@@ -297,7 +299,7 @@ def clock_breakdown(cfg, tile, step, torch, ch, nat, runs=5):
                 off += n
                 wall = s[:, 2] - s[:, 1]
                 cyc = s[:, 5] - s[:, 4]
-                ideal = 2.0 * tile[0] * tile[1] * (cfg.widths[l] / nsplit[l]) / 4096.0
+                ideal = 2.0 * tile[0] * tile[1] * (cfg.widths[l] / nsplit[l]) / 4096.0 * per_cu
                 j = (np.arange(n) // nsplit[l]) % nbn
                 ghz.append(cyc / wall * 0.1)
                 frac.append(ideal / cyc)
@@ -306,7 +308,7 @@ def clock_breakdown(cfg, tile, step, torch, ch, nat, runs=5):
     by_q = [round(float(np.median(ghz[queue == q])), 3) for q in range(nq)]
     med = float(np.median(ghz))
     out = {"shader_ghz_median": round(med, 3), "shader_ghz_by_queue": by_q,
-           "mfma_cycle_frac_median": round(float(np.median(frac)), 3),
+           "mfma_cycle_frac_median": round(float(np.median(frac)), 3), "workgroups_per_cu": per_cu,
            "bf16_peak_at_median_clock_tflops": round(256 * 4096 * med * 1e9 / 1e12, 1),
            "runs": runs, "source": "CP_FLAG_TRACE shader-clock and wall-clock stamps per tile"}
     log("clock", out)
