@@ -158,6 +158,7 @@ struct cp_chain {
         int nq = 1;
         int32_t qbase[cp::kMaxQueues] = {}, qsize[cp::kMaxQueues] = {}, qfirst[cp::kMaxQueues] = {};
         int32_t qworkers[cp::kMaxQueues] = {};
+        int32_t first_formula = 0;     // pre-filled slots follow cp::first_item
         uint32_t *d_qinit = nullptr;   // initial queue image
     } lay[2];
     int copy_layout[2] = {0, 0};       // layout each per-run state copy was reset for
@@ -281,6 +282,7 @@ cp::ChainArgs make_args(const cp_chain *p, const void *X, const void *const *W, 
         a.qfirst[q] = ly.qfirst[q];
         a.qworkers[q] = ly.qworkers[q];
     }
+    a.first_formula = fixed_queue < 0 ? ly.first_formula : 0;
     a.qinit = ly.d_qinit;
     const int c = copy, n = copy ^ 1;
     a.queue = p->d_queue[c];
@@ -507,6 +509,15 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
             std::copy(first[q].begin(), first[q].end(), qinit.begin() + base);
             base += size[q];
         }
+        // the kernel computes a worker's pre-filled first slot instead of
+        // reading it; use that only where the formula reproduces the image
+        lx.first_formula = 1;
+        for (int q = 0; q < lx.nq && lx.first_formula; ++q)
+            for (size_t r = 0; r < first[q].size(); ++r)
+                if (cp::first_item(g.nbn[0] * g.nsplit[0], lx.nq, q, (uint32_t)r) != first[q][r]) {
+                    lx.first_formula = 0;
+                    break;
+                }
         CP_HIP(hipMemcpy(lx.d_qinit, qinit.data(), T * 4, hipMemcpyHostToDevice));
         // spatial layout: queue l holds layer l's tiles (layer 0 pre-filled,
         // row-block-major).  Layer l runs on CU set l mod 2, so every layer's

@@ -63,6 +63,8 @@ struct ChainArgs {
     int32_t qbase[kMaxQueues];   // first slot of each queue in `queue`
     int32_t qsize[kMaxQueues];   // tiles owned by each queue
     int32_t qfirst[kMaxQueues];  // of which first-layer tiles (pre-filled)
+    int32_t first_formula;   // 1: slot r < qfirst[q] of queue q holds first_item(q, r), so a
+                             // worker's static first slot needs no queue read (checked at plan)
     uint32_t *queue;     // [T] slots of all queues (kEmpty until pushed)
     uint32_t *ctl;       // [kCtlWords] per-queue head / tail, status
     int32_t *score;      // [T] remaining producers per tile
@@ -88,6 +90,16 @@ struct ChainArgs {
 // split) modulo nq, so the items of one tile spread over the queues.
 __host__ __device__ inline int owner_queue(const LayerDesc &d, int id, int nq) {
     return ((id - d.tile_off) % (d.nbn * d.nsplit)) % nq;
+}
+
+// The r-th pre-filled (first-layer) item of queue q, r < qfirst[q]: the
+// queue image lists, row-block by row-block, the items whose position in
+// the row-block (column panel x nsplit + split, `per` of them) is q modulo
+// nq.  Row-block i holds ceil((per - q) / nq) of them.
+__host__ __device__ inline uint32_t first_item(int per, int nq, int q, uint32_t r) {
+    const uint32_t in_rb = (uint32_t)((per - q + nq - 1) / nq);
+    const uint32_t i = r / in_rb, k = r - i * in_rb;
+    return i * (uint32_t)per + (uint32_t)q + k * (uint32_t)nq;
 }
 
 // A compiled kernel variant (element type x tile shape).

@@ -661,6 +661,17 @@ __device__ uint32_t take_ticket(const ChainArgs &a, int q) {
     return __hip_atomic_fetch_add(a.ctl + ctl_head(q), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Debug and trace bookkeeping of a dequeue: count it, stamp it.
+__device__ __forceinline__ void dequeued(const ChainArgs &a, uint32_t id, uint64_t t0) {
+    if (a.deq_count)
+        __hip_atomic_fetch_add(a.deq_count + id, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (a.trace) {
+        a.trace[kTraceWords * (size_t)id + 0] = t0;
+        a.trace[kTraceWords * (size_t)id + 1] = wall_clock64();
+        a.trace[kTraceWords * (size_t)id + 4] = clock64();
+    }
+}
+
 __device__ uint32_t wait_slot(const ChainArgs &a, int q, uint32_t t) {
     if (t >= (uint32_t)a.qsize[q]) return kDone;
     const uint32_t *slot = a.queue + a.qbase[q] + t;
@@ -689,13 +700,18 @@ __device__ uint32_t wait_slot(const ChainArgs &a, int q, uint32_t t) {
         // stores reached memory before any counter was decremented.
         (void)__hip_atomic_load(a.score + id, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (a.deq_count)
-        __hip_atomic_fetch_add(a.deq_count + id, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (a.trace) {
-        a.trace[kTraceWords * (size_t)id + 0] = t0;
-        a.trace[kTraceWords * (size_t)id + 1] = wall_clock64();
-        a.trace[kTraceWords * (size_t)id + 4] = clock64();
-    }
+    dequeued(a, id, t0);
+    return id;
+}
+
+// A worker's first slot is its own (no ticket atomic) and, for the
+// pre-filled first-layer slots, its content is known: compute it instead
+// of reading it, which saves the first tile a memory round trip.
+__device__ uint32_t first_slot(const ChainArgs &a, int q, uint32_t t) {
+    if (!a.first_formula || t >= (uint32_t)a.qfirst[q]) return wait_slot(a, q, t);
+    const uint64_t t0 = a.trace ? wall_clock64() : 0;
+    const uint32_t id = first_item(a.layer[0].nbn * a.layer[0].nsplit, a.nq, q, t);
+    dequeued(a, id, t0);
     return id;
 }
 
@@ -808,10 +824,11 @@ constexpr int kSchedLane = 64;
 // XCDs serve the queue of their own XCD) is exhausted.  The grid is the
 // number of workgroups the device holds at once, so on an otherwise idle
 // device every worker is resident (a cooperative launch guarantees it).
-// First, the workers reset the other copy of the per-run state for the next
-// run (nothing of this run reads it; the kernel boundary publishes it).  The
-// tile ID is broadcast through the first word of stage 0; the second barrier
-// guarantees every thread has read it before the body's loads reuse stage 0.
+// On the way out the workers reset the other copy of the per-run state for
+// the next run (nothing of this run reads it; the kernel boundary publishes
+// it).  The tile ID is broadcast through the first word of stage 0; the
+// second barrier guarantees every thread has read it before the body's
+// loads reuse stage 0.
 template <class Body, bool SPLIT>
 __global__ void __launch_bounds__(Body::NT) worker_kernel(ChainArgs a) {
     char *stg[5];
@@ -819,12 +836,13 @@ __global__ void __launch_bounds__(Body::NT) worker_kernel(ChainArgs a) {
     volatile uint32_t *slot = reinterpret_cast<volatile uint32_t *>(stg[0]);
     const int q = a.fixed_queue >= 0 ? a.fixed_queue : (int)(blockIdx.x % (unsigned)a.nq);
     const bool sched = threadIdx.x == kSchedLane;
-    reset_copy(a, a.nxt_queue, a.nxt_ctl, a.nxt_score, a.nxt_deq_count, a.nxt_trace, a.nxt_arrive);
     // first slot without an atomic: the r-th worker of queue q owns slot r
     // (the reset set each head past the workers' count)
     uint32_t ticket = a.fixed_queue >= 0 ? blockIdx.x : blockIdx.x / (unsigned)a.nq;
+    bool first = true;
     for (;;) {
-        if (sched) *slot = wait_slot(a, q, ticket);
+        if (sched) *slot = first ? first_slot(a, q, ticket) : wait_slot(a, q, ticket);
+        first = false;
         __syncthreads();
         // the broadcast ID is uniform; saying so keeps the layer descriptor
         // and the buffer resources derived from it in scalar registers
@@ -833,8 +851,8 @@ __global__ void __launch_bounds__(Body::NT) worker_kernel(ChainArgs a) {
         if (id >= (uint32_t)a.T) break;
         int l, i, j, split;
         decode(a, id, l, i, j, split);
-        const uint32_t first = id - (uint32_t)split;  // the tile's first item carries its edges
-        const bool done = Body::template run<SPLIT>(a.layer[l], i, j, split, a.arrive + first, stg, [&] {
+        const uint32_t first_item_id = id - (uint32_t)split;  // the tile's first item carries its edges
+        const bool done = Body::template run<SPLIT>(a.layer[l], i, j, split, a.arrive + first_item_id, stg, [&] {
             if (sched) ticket = take_ticket(a, q);
         });
         if (a.trace && threadIdx.x == 0) {
@@ -844,9 +862,14 @@ __global__ void __launch_bounds__(Body::NT) worker_kernel(ChainArgs a) {
         // after publish's opening barrier wave 0 releases the tile while the
         // scheduler lane (wave 1) already waits for the next one; a split-K
         // item that did not complete its tile has nothing to release
-        if (done && l + 1 < a.L) publish(a, first, l);
+        if (done && l + 1 < a.L) publish(a, first_item_id, l);
         else __syncthreads();
     }
+    // Reset the other copy of the per-run state for the next run: nothing of
+    // this run reads it, and the kernel boundary publishes it.  Done on the
+    // way out, where a worker has nothing left to wait for, rather than
+    // ahead of its first tile.
+    reset_copy(a, a.nxt_queue, a.nxt_ctl, a.nxt_score, a.nxt_deq_count, a.nxt_trace, a.nxt_arrive);
 }
 
 // One layer, one tile per workgroup, row-blocks [rb0, rb0 + nrb): the plain
