@@ -268,7 +268,7 @@ def gpu_state():
 
 
 def clock_breakdown(cfg, tile, step, torch, ch, nat, runs=5):
-    """Shader clock and MFMA cycle efficiency of the tile bodies, from the
+    """Protocol phases, shader clock and MFMA cycle efficiency of the tile bodies, from the
     per-tile trace (CP_FLAG_TRACE) of a few back-to-back pipelined runs: a
     tile's clock is its shader-clock cycles over its wall-clock span, its
     MFMA cycle fraction the cycles a compute unit needs at the bf16 MFMA
@@ -286,11 +286,30 @@ def clock_breakdown(cfg, tile, step, torch, ch, nat, runs=5):
         nq = st["n_queues"]
         for _ in range(10):
             step(p=pt)
+        g = nat.cp_chain_tile_graph(cfg.M, cfg.widths, tile[0], tile[1], nsplit=nsplit)
+        dep_off, dep_ids = np.array(g["dep_off"]), np.array(g["dep_ids"])
+        src = np.repeat(np.arange(len(dep_off) - 1), np.diff(dep_off))   # producer of each edge
         ghz, frac, queue = [], [], []
+        t_rel, t_deq, t_wait = [], [], []
         for _ in range(runs):
             step(p=pt)
             pt.stats()
             tr = np.array(pt.trace(), dtype=np.uint64).reshape(-1, nat.CP_TRACE_WORDS).astype(np.int64)
+            # protocol phases (100 MHz ticks -> us): a producer's release after
+            # its body; a consumer's dequeue after the last release among its
+            # producers; the time a worker's slot waited for a tile
+            if len(dep_ids):
+                prod = np.unique(src)
+                # a split tile's edges and release sit on its first item; its
+                # body ends when the last of its items ends
+                lay = np.searchsorted(g["layer_off"], prod, side="right") - 1
+                body_end = np.array([tr[p:p + nsplit[l], 2].max() for p, l in zip(prod, lay)])
+                t_rel.append((tr[prod, 3] - body_end) / 100.0)
+                last = np.full(len(tr), -1, dtype=np.int64)
+                np.maximum.at(last, dep_ids, tr[src, 3])
+                cons = np.nonzero(last >= 0)[0]
+                t_deq.append((tr[cons, 1] - last[cons]) / 100.0)
+                t_wait.append((tr[cons, 1] - tr[cons, 0]) / 100.0)
             off = 0
             for l in range(L):
                 nbn = cfg.widths[l + 1] // tile[1]
@@ -311,6 +330,14 @@ def clock_breakdown(cfg, tile, step, torch, ch, nat, runs=5):
            "mfma_cycle_frac_median": round(float(np.median(frac)), 3), "workgroups_per_cu": per_cu,
            "bf16_peak_at_median_clock_tflops": round(256 * 4096 * med * 1e9 / 1e12, 1),
            "runs": runs, "source": "CP_FLAG_TRACE shader-clock and wall-clock stamps per tile"}
+    if t_rel:
+        t_rel, t_deq, t_wait = np.concatenate(t_rel), np.concatenate(t_deq), np.concatenate(t_wait)
+        out["protocol_us"] = {
+            "release_after_body_median": round(float(np.median(t_rel)), 2),
+            "release_after_body_max": round(float(t_rel.max()), 2),
+            "dequeue_after_last_producer_release_median": round(float(np.median(t_deq)), 2),
+            "dequeue_after_last_producer_release_max": round(float(t_deq.max()), 2),
+            "consumer_slot_wait_median": round(float(np.median(t_wait)), 2)}
     log("clock", out)
     return out
 

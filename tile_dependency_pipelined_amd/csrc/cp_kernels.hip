@@ -937,9 +937,24 @@ hipError_t launch_layer_t(const ChainArgs &a, int l, int rb0, int nrb, hipStream
     return hipGetLastError();
 }
 
+// Workgroups of the persistent worker one compute unit holds at once.  A
+// plan sizes its grid before it knows whether it will launch the split-K
+// instantiation, whose register use differs, so this is the smaller of the
+// two instantiations' figures: every worker of either is then resident,
+// which the queue protocol's forward progress relies on.
 template <class Body>
 hipError_t occupancy_t(int *blocks) {
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, worker_kernel<Body, false>, Body::NT, 0);
+    int plain = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&plain, worker_kernel<Body, false>, Body::NT, 0);
+    if (e != hipSuccess) return e;
+    *blocks = plain;
+    if constexpr (!std::is_same<Body, F32Body>::value) {
+        int split = 0;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&split, worker_kernel<Body, true>, Body::NT, 0);
+        if (e != hipSuccess) return e;
+        *blocks = split < plain ? split : plain;
+    }
+    return hipSuccess;
 }
 
 // LDS stages per tile shape: as many as fit the occupancy each shape aims for
