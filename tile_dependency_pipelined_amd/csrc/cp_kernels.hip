@@ -490,8 +490,8 @@ struct Bf16Body {
 };
 
 // ----------------------------------------------------------------------------
-// fp32 tile body (64 x 64, BK = 32) on v_mfma_f32_32x32x2_f32, two stages,
-// register-staged.  Small chains only; A is transposed into LDS ([k][m],
+// fp32 tile body (64 x 64, BK = 32) on v_mfma_f32_32x32x2_f32, two LDS
+// stages fed from a ring of four register-staged slabs.  Small chains only; A is transposed into LDS ([k][m],
 // padded) so that both fragment reads are lane-contiguous.
 // ----------------------------------------------------------------------------
 struct F32Body {
@@ -517,29 +517,46 @@ struct F32Body {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
 
-        float4 ra[2], rb[2];
-        auto gload = [&](int k0) {
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int r = q * 32 + (tid >> 3), c4 = tid & 7;
-                ra[q] = *reinterpret_cast<const float4 *>(A + (size_t)(row0 + r) * K + k0 + c4 * 4);
-                const int k = q * 16 + (tid >> 4), n4 = tid & 15;
-                rb[q] = *reinterpret_cast<const float4 *>(W + (size_t)(k0 + k) * N + col0 + n4 * 4);
-            }
+        // Register ring of D slabs: the global loads of slabs ks+1 .. ks+D-1
+        // are in flight while slab ks is multiplied out of LDS, so a tile pays
+        // the load latency about once instead of once per slab.
+        // The ring is four named slabs chosen at compile time (no array), so
+        // that every slab stays in registers.
+        constexpr int D = 4;
+        struct Slab {
+            float4 a0, a1, b0, b1;
         };
-        auto lstore = [&](char *st) {
+        Slab r0, r1, r2, r3;
+        auto ring = [&](auto U) -> Slab & {
+            constexpr int u = decltype(U)::value;
+            if constexpr (u == 0) return r0;
+            else if constexpr (u == 1) return r1;
+            else if constexpr (u == 2) return r2;
+            else return r3;
+        };
+        auto gload = [&](int k0, Slab &sl) {
+            const int r = tid >> 3, c4 = tid & 7;
+            sl.a0 = *reinterpret_cast<const float4 *>(A + (size_t)(row0 + r) * K + k0 + c4 * 4);
+            sl.a1 = *reinterpret_cast<const float4 *>(A + (size_t)(row0 + 32 + r) * K + k0 + c4 * 4);
+            const int k = tid >> 4, n4 = tid & 15;
+            sl.b0 = *reinterpret_cast<const float4 *>(W + (size_t)(k0 + k) * N + col0 + n4 * 4);
+            sl.b1 = *reinterpret_cast<const float4 *>(W + (size_t)(k0 + 16 + k) * N + col0 + n4 * 4);
+        };
+        auto lstore = [&](char *st, const Slab &sl) {
             float *As = reinterpret_cast<float *>(st);
             float *Bs = As + BK * AP;
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int r = q * 32 + (tid >> 3), c4 = tid & 7;
-                As[(c4 * 4 + 0) * AP + r] = ra[q].x;
-                As[(c4 * 4 + 1) * AP + r] = ra[q].y;
-                As[(c4 * 4 + 2) * AP + r] = ra[q].z;
-                As[(c4 * 4 + 3) * AP + r] = ra[q].w;
-                const int k = q * 16 + (tid >> 4), n4 = tid & 15;
-                *reinterpret_cast<float4 *>(Bs + k * BP + n4 * 4) = rb[q];
-            }
+            const int r = tid >> 3, c4 = tid & 7;
+            As[(c4 * 4 + 0) * AP + r] = sl.a0.x;
+            As[(c4 * 4 + 1) * AP + r] = sl.a0.y;
+            As[(c4 * 4 + 2) * AP + r] = sl.a0.z;
+            As[(c4 * 4 + 3) * AP + r] = sl.a0.w;
+            As[(c4 * 4 + 0) * AP + 32 + r] = sl.a1.x;
+            As[(c4 * 4 + 1) * AP + 32 + r] = sl.a1.y;
+            As[(c4 * 4 + 2) * AP + 32 + r] = sl.a1.z;
+            As[(c4 * 4 + 3) * AP + 32 + r] = sl.a1.w;
+            const int k = tid >> 4, n4 = tid & 15;
+            *reinterpret_cast<float4 *>(Bs + k * BP + n4 * 4) = sl.b0;
+            *reinterpret_cast<float4 *>(Bs + (16 + k) * BP + n4 * 4) = sl.b1;
         };
         auto compute = [&](const char *st) {
             const float *As = reinterpret_cast<const float *>(st);
@@ -554,16 +571,34 @@ struct F32Body {
         };
 
         const int nk = K / BK;
-        gload(0);
-        lstore(stg[0]);
+        // slabs past the last one re-load the last slab (in bounds, unused)
+        gload(0, r0);
+        gload((1 < nk ? 1 : nk - 1) * BK, r1);
+        gload((2 < nk ? 2 : nk - 1) * BK, r2);
+        gload((3 < nk ? 3 : nk - 1) * BK, r3);
+        lstore(stg[0], r0);
         __syncthreads();
-        for (int ks = 0; ks < nk; ++ks) {
+        // slab ks sits in LDS stage ks mod 2 and its ring slot u = ks mod D is
+        // free again: refill it with slab ks + D, multiply slab ks, move slab
+        // ks + 1 from its ring slot into the other stage
+        auto step = [&](auto U, int ks) {
+            constexpr int u = decltype(U)::value, un = (u + 1) % D;
             char *cur = (ks & 1) ? stg[1] : stg[0], *nxt = (ks & 1) ? stg[0] : stg[1];  // no dynamic indexing
-            if (ks + 1 < nk) gload((ks + 1) * BK);
+            gload((ks + D < nk ? ks + D : nk - 1) * BK, ring(ic<u>{}));
             compute(cur);
-            if (ks + 1 < nk) lstore(nxt);
+            if (ks + 1 < nk) lstore(nxt, ring(ic<un>{}));
             __syncthreads();
+        };
+        int ks = 0;
+        for (; ks + D <= nk; ks += D) {
+            step(ic<0>{}, ks);
+            step(ic<1>{}, ks + 1);
+            step(ic<2>{}, ks + 2);
+            step(ic<3>{}, ks + 3);
         }
+        if (ks < nk) step(ic<0>{}, ks++);
+        if (ks < nk) step(ic<1>{}, ks++);
+        if (ks < nk) step(ic<2>{}, ks++);
         before_epilogue();
 
         const int act = d.act;
