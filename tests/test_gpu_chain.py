@@ -110,7 +110,17 @@ def test_c1_fp32_parity_all_modes(rt):
     assert same_bits(out["pipelined"], out["sequential"])
     assert same_bits(out["pipelined"], out["microbatch"])
     assert same_bits(out["pipelined"], out["spatial"])
-    assert st["n_tiles"] == 32 and st["n_edges"] == 128
+    # 16 tiles per layer leave most compute units idle, so the plan splits
+    # both fp32 layers along k (items of 64 k, k-range dependencies)
+    assert st["nsplit"][0] > 1 and st["nsplit"][1] > 1, st["nsplit"]
+    assert st["nonzero_arrivals"] == 0
+    # unsplit, the plan uses exactly the hand-derived C1 tile graph
+    nat = rt["nat"]
+    out1, st1 = run_modes(rt, X, Ws, cfg.dtype, cfg.tile, flags=all_flags() | nat.CP_FLAG_NO_SPLIT,
+                          modes=("pipelined", "sequential"), reps=2)
+    assert st1["n_tiles"] == 32 and st1["n_edges"] == 128
+    assert oracle.rel_err(as_values(out1["pipelined"], cfg.dtype), ref) <= TOL[gen.F32]
+    assert same_bits(out1["pipelined"], out1["sequential"])
 
 
 # ----------------------------------------------------------------------------- bf16 small

@@ -128,10 +128,13 @@ void choose_splits(int64_t M, int32_t L, const int64_t *widths, int32_t tile_m, 
     const int64_t nrb = M / tile_m;
     for (int l = 0; l < L; ++l) {
         ns[l] = 1;
-        if (!allow || dtype != CP_BF16) continue;
+        if (!allow) continue;
+        // an item keeps at least 16 slabs of 64 k (bf16) or 2 slabs of 32 k
+        // (fp32: its small tiles leave most of the device idle otherwise)
+        const int64_t min_slabs = dtype == CP_BF16 ? 16 : 2;
         const int64_t tiles = nrb * (widths[l + 1] / tile_n), slabs = widths[l] / k_step;
         const int64_t prod_tiles = l > 0 ? widths[l] / tile_n : 0;
-        while (tiles * 2 * ns[l] <= capacity && slabs % (2 * ns[l]) == 0 && slabs / (2 * ns[l]) >= 16 &&
+        while (tiles * 2 * ns[l] <= capacity && slabs % (2 * ns[l]) == 0 && slabs / (2 * ns[l]) >= min_slabs &&
                (l == 0 || prod_tiles % (2 * ns[l]) == 0))
             ns[l] *= 2;
     }

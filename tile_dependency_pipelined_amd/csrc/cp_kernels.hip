@@ -500,15 +500,20 @@ struct F32Body {
     static constexpr int BP = BN + 4;  // padded W row ([k][n]), keeps 16-byte alignment
     static constexpr int STAGE = (BK * AP + BK * BP) * 4;
 
-    // `before_epilogue` as in Bf16Body; no split-K (plans never split fp32
-    // layers), so every call completes its tile.
+    // `before_epilogue` and split-K as in Bf16Body: with d.nsplit > 1 this
+    // item multiplies k in [split K / nsplit, (split + 1) K / nsplit), stores
+    // an fp32 partial, and the last item of the tile to arrive sums all
+    // partials in split order and runs the epilogue.  Returns whether this
+    // call completed the tile.
     template <bool SPLIT, class Hook>
-    __device__ __forceinline__ static bool run(const LayerDesc &d, int i, int j, int /*split*/,
-                                               uint32_t * /*arrive*/, char *const *stg, Hook &&before_epilogue) {
-        const float *__restrict__ A = static_cast<const float *>(d.A);
-        const float *__restrict__ W = static_cast<const float *>(d.W);
-        float *__restrict__ C = static_cast<float *>(d.C);
+    __device__ __forceinline__ static bool run(const LayerDesc &d, int i, int j, int split, uint32_t *arrive,
+                                               char *const *stg, Hook &&before_epilogue) {
         const int K = d.K, N = d.N;
+        const int kspan = SPLIT ? __builtin_amdgcn_readfirstlane(K / d.nsplit) : K;
+        const int kbeg = SPLIT ? __builtin_amdgcn_readfirstlane(split * kspan) : 0;
+        const float *__restrict__ A = static_cast<const float *>(d.A) + kbeg;
+        const float *__restrict__ W = static_cast<const float *>(d.W) + (size_t)kbeg * N;
+        float *__restrict__ C = static_cast<float *>(d.C);
         const int row0 = i * BM, col0 = j * BN;
         const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
         const int wm = wave >> 1, wn = wave & 1;
@@ -570,7 +575,7 @@ struct F32Body {
             }
         };
 
-        const int nk = K / BK;
+        const int nk = kspan / BK;
         // slabs past the last one re-load the last slab (in bounds, unused)
         gload(0, r0);
         gload((1 < nk ? 1 : nk - 1) * BK, r1);
@@ -600,6 +605,61 @@ struct F32Body {
         if (ks < nk) step(ic<1>{}, ks++);
         if (ks < nk) step(ic<2>{}, ks++);
         before_epilogue();
+
+        if (SPLIT && d.nsplit > 1) {
+            // Partial tile in fragment-native layout [wave][h][lane][2]
+            // floats, stored at agent scope (write-through); every wave waits
+            // for its stores before the barrier, so they are all in memory
+            // before the arrival count is raised.
+            const int tile = i * d.nbn + j;
+            float *ws = d.ws + (size_t)(tile * d.nsplit + split) * (BM * BN);
+#pragma unroll
+            for (int h = 0; h < 8; ++h) {
+                const uint64_t v = (uint64_t)__float_as_uint(acc[2 * h]) |
+                                   ((uint64_t)__float_as_uint(acc[2 * h + 1]) << 32);
+                __hip_atomic_store(reinterpret_cast<uint64_t *>(ws + ((wave * 8 + h) * 64 + lane) * 2), v,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            wait_vmcnt<0>();
+            __syncthreads();
+            volatile uint32_t *word = reinterpret_cast<volatile uint32_t *>(stg[0]) + 1;
+            if (tid == 0)
+                *word = __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __syncthreads();
+            const bool last = *word == (uint32_t)(d.nsplit - 1);
+            __syncthreads();  // everyone has read the word before the LDS is reused
+            if (!last) return false;
+            // Last to arrive: reset the count for the next run and sum all
+            // partials (its own included, read back) in split order, at
+            // agent scope, up to four partials' loads in flight at once.
+            if (tid == 0) __hip_atomic_store(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const float *ws0 = d.ws + (size_t)(tile * d.nsplit) * (BM * BN) + ((size_t)wave * 8 * 64 + lane) * 2;
+            const int ns = d.nsplit;
+            constexpr int G = 4;
+            for (int k0 = 0; k0 < ns; k0 += G) {
+                uint64_t v[G][8];
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const int k = k0 + g < ns ? k0 + g : ns - 1;  // in range; unused past ns
+#pragma unroll
+                    for (int h = 0; h < 8; ++h)
+                        v[g][h] = __hip_atomic_load(
+                            reinterpret_cast<const uint64_t *>(ws0 + (size_t)k * (BM * BN) + h * 128),
+                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    if (k0 + g >= ns) break;
+#pragma unroll
+                    for (int h = 0; h < 8; ++h) {
+                        const float v0 = __uint_as_float((uint32_t)v[g][h]);
+                        const float v1 = __uint_as_float((uint32_t)(v[g][h] >> 32));
+                        acc[2 * h] = k0 + g == 0 ? v0 : acc[2 * h] + v0;
+                        acc[2 * h + 1] = k0 + g == 0 ? v1 : acc[2 * h + 1] + v1;
+                    }
+                }
+            }
+        }
 
         const int act = d.act;
         const int m = row0 + wm * 32 + (lane & 31);
@@ -949,13 +1009,12 @@ hipError_t launch_worker_s(const ChainArgs &a, int grid, bool cooperative, hipSt
                                       dim3(Body::NT), args, 0, s);
 }
 
-// Split-K instantiations exist only for bf16 bodies (fp32 layers never split).
+// A plan with a split layer launches the split-K instantiation.
 template <class Body>
 hipError_t launch_worker_t(const ChainArgs &a, int grid, bool cooperative, hipStream_t s) {
     bool split = false;
     for (int l = 0; l < a.L; ++l) split |= a.layer[l].nsplit > 1;
-    if constexpr (!std::is_same<Body, F32Body>::value)
-        if (split) return launch_worker_s<Body, true>(a, grid, cooperative, s);
+    if (split) return launch_worker_s<Body, true>(a, grid, cooperative, s);
     return launch_worker_s<Body, false>(a, grid, cooperative, s);
 }
 
@@ -963,11 +1022,10 @@ template <class Body>
 hipError_t launch_layer_t(const ChainArgs &a, int l, int rb0, int nrb, hipStream_t s) {
     const int grid = nrb * a.layer[l].nbn * a.layer[l].nsplit;
     if (grid <= 0) return hipSuccess;
-    if constexpr (!std::is_same<Body, F32Body>::value)
-        if (a.layer[l].nsplit > 1) {
-            hipLaunchKernelGGL((layer_kernel<Body, true>), dim3(grid), dim3(Body::NT), 0, s, a, l, rb0);
-            return hipGetLastError();
-        }
+    if (a.layer[l].nsplit > 1) {
+        hipLaunchKernelGGL((layer_kernel<Body, true>), dim3(grid), dim3(Body::NT), 0, s, a, l, rb0);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL((layer_kernel<Body, false>), dim3(grid), dim3(Body::NT), 0, s, a, l, rb0);
     return hipGetLastError();
 }
@@ -982,13 +1040,10 @@ hipError_t occupancy_t(int *blocks) {
     int plain = 0;
     hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&plain, worker_kernel<Body, false>, Body::NT, 0);
     if (e != hipSuccess) return e;
-    *blocks = plain;
-    if constexpr (!std::is_same<Body, F32Body>::value) {
-        int split = 0;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&split, worker_kernel<Body, true>, Body::NT, 0);
-        if (e != hipSuccess) return e;
-        *blocks = split < plain ? split : plain;
-    }
+    int split = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&split, worker_kernel<Body, true>, Body::NT, 0);
+    if (e != hipSuccess) return e;
+    *blocks = split < plain ? split : plain;
     return hipSuccess;
 }
 
