@@ -192,11 +192,19 @@ def main():
 
     if not args.profile:
         result["gpu_state_after_timed_steps"] = gpu_state()
+    # diagnostics: a failure in one of them is reported in the line, never
+    # allowed to lose the measurement above
     if not args.profile and cfg.dtype == gen.BF16:
-        result["clock"] = clock_breakdown(cfg, tile, step, torch, ch, nat)
+        try:
+            result["clock"] = clock_breakdown(cfg, tile, step, torch, ch, nat)
+        except Exception as e:
+            result["clock"] = {"error": f"{type(e).__name__}: {e}"[:300]}
 
     if not args.no_cpu_baseline and not args.profile:
-        result["cpu_baseline"] = cpu_baseline(cfg, X, Ws, args.cpu_sample_rows)
+        try:
+            result["cpu_baseline"] = cpu_baseline(cfg, X, Ws, args.cpu_sample_rows)
+        except Exception as e:
+            result["cpu_baseline"] = {"error": f"{type(e).__name__}: {e}"[:300]}
 
     plan.close()
     print(json.dumps(result), flush=True)
