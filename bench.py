@@ -167,13 +167,7 @@ def main():
         del a, b
 
     traffic = traffic_from_profile(cfg.key, tile)
-    # the roofline that bounds the chain: MFMA above the ridge point (peak
-    # flop/s over peak HBM bytes/s), HBM below it (C5: 254 flop/B < 312.5)
-    intensity = flops / cfg.min_bytes()
-    if intensity >= peak * 1e12 / (PEAK_HBM_GBS * 1e9):
-        bound, achieved, peak_b, unit = "mfma", kernel_tflops, peak, "TFLOP/s"
-    else:
-        bound, achieved, peak_b, unit = "hbm", cfg.min_bytes() / (kernel_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
+    bound, achieved, peak_b, unit, intensity = roofline(flops, cfg.min_bytes(), kernel_ms, peak)
     result["roofline"] = {
         "bound": bound, "achieved": round(achieved, 2), "peak": peak_b, "unit": unit,
         "frac": round(achieved / peak_b, 4), "tflops": round(kernel_tflops, 2),
@@ -208,6 +202,17 @@ def main():
 
     plan.close()
     print(json.dumps(result), flush=True)
+
+
+def roofline(flops, min_bytes, launch_ms, peak_tflops):
+    """The roofline that bounds a launch: MFMA at or above the ridge point
+    (peak flop/s over peak HBM bytes/s), HBM below it.  Returns (bound,
+    achieved, peak, unit, flop per byte); achieved is algorithmic flops or
+    algorithmic bytes per launch over the launch time."""
+    intensity = flops / min_bytes
+    if intensity >= peak_tflops * 1e12 / (PEAK_HBM_GBS * 1e9):
+        return "mfma", flops / (launch_ms * 1e-3) / 1e12, peak_tflops, "TFLOP/s", intensity
+    return "hbm", min_bytes / (launch_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s", intensity
 
 
 def compare_modes(plan, step, stream, cfg, tile, reps, torch, tuning):

@@ -231,3 +231,25 @@ def test_plan_without_device_reports_no_device():
 def test_destroy_null_is_noop():
     assert nat.lib().cp_chain_destroy(None) == 0
     assert nat.lib().cp_chain_run(None, None, None, None, None, 0, 0) == nat.CP_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("key,bound", [("c1", "mfma"), ("c2", "mfma"), ("c3", "mfma"), ("c4", "mfma"),
+                                       ("c5", "hbm")])
+def test_bench_roofline_bound(key, bound):
+    """The benchmark reports the roofline that bounds each workload: its
+    arithmetic intensity (algorithmic flops over X + sum W + Y bytes) against
+    the ridge point of the element type's peak and 8 TB/s.  C5 (254 flop/B)
+    sits below the bf16 ridge (312.5 flop/B); the others above theirs."""
+    import bench
+    cfg = gen.CONFIGS[key]
+    peak = bench.PEAK_BF16_TFLOPS if cfg.dtype == gen.BF16 else bench.PEAK_FP32_TFLOPS
+    b, achieved, peak_b, unit, intensity = bench.roofline(cfg.flops, cfg.min_bytes(), 1.0, peak)
+    assert b == bound
+    if b == "hbm":
+        assert unit == "GB/s" and peak_b == bench.PEAK_HBM_GBS
+        assert achieved == pytest.approx(cfg.min_bytes() / 1e-3 / 1e9)
+    else:
+        assert unit == "TFLOP/s" and peak_b == peak
+        assert achieved == pytest.approx(cfg.flops / 1e-3 / 1e12)
+    if key == "c5":
+        assert intensity == pytest.approx(253.7, abs=0.5)
