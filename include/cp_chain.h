@@ -72,7 +72,7 @@ typedef struct cp_chain cp_chain; /* opaque plan */
 
 /* plan flags (bitmask) */
 #define CP_FLAG_DEBUG 1u        /* count dequeues per tile; enables invariant checks in stats */
-#define CP_FLAG_TRACE 2u        /* per-tile timestamps (100 MHz wall clock)                  */
+#define CP_FLAG_TRACE 2u        /* per-tile timestamps (wall clock, shader clock)            */
 #define CP_FLAG_POISON 4u       /* fill intermediates with NaN before every run              */
 #define CP_FLAG_DELAY_INJECT 8u /* a fixed pseudo-random quarter of producers stall ~20 us   */
 /* test only: the last tile's in-degree is raised by one so that it never

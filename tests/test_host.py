@@ -34,12 +34,14 @@ def test_header_constants_match_binding():
     for name in ("CP_F32", "CP_BF16", "CP_ACT_NONE", "CP_ACT_GELU_TANH", "CP_MODE_PIPELINED",
                  "CP_MODE_SEQUENTIAL", "CP_MODE_MICROBATCH", "CP_OK", "CP_ERR_INVALID_ARG",
                  "CP_ERR_SHAPE", "CP_ERR_UNSUPPORTED", "CP_ERR_OOM", "CP_ERR_HIP", "CP_ERR_TIMEOUT",
-                 "CP_ERR_NO_DEVICE", "CP_ERR_INVARIANT", "CP_MAX_LAYERS"):
+                 "CP_ERR_NO_DEVICE", "CP_ERR_INVARIANT", "CP_MAX_LAYERS", "CP_MODE_SPATIAL",
+                 "CP_TRACE_WORDS"):
         m = re.search(rf"#define\s+{name}\s+\(?(-?\d+)\)?", src)
         assert m, name
         assert int(m.group(1)) == getattr(nat, name), name
     for name in ("CP_FLAG_DEBUG", "CP_FLAG_TRACE", "CP_FLAG_POISON", "CP_FLAG_DELAY_INJECT",
-                 "CP_FLAG_STARVE_LAST"):
+                 "CP_FLAG_STARVE_LAST", "CP_FLAG_EAGER", "CP_FLAG_COOPERATIVE", "CP_FLAG_FENCE_RELEASE",
+                 "CP_FLAG_TIMING", "CP_FLAG_NO_SPLIT"):
         m = re.search(rf"#define\s+{name}\s+(\d+)u", src)
         assert m and int(m.group(1)) == getattr(nat, name), name
 
