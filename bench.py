@@ -188,6 +188,11 @@ def main():
         result["gpu_state_after_timed_steps"] = gpu_state()
     # diagnostics: a failure in one of them is reported in the line, never
     # allowed to lose the measurement above
+    if not args.profile and not args.no_modes and cfg.dtype == gen.BF16:
+        try:
+            result["context_vendor_gemm"] = vendor_gemm_chain(cfg, dX, dW, stream, torch)
+        except Exception as e:
+            result["context_vendor_gemm"] = {"error": f"{type(e).__name__}: {e}"[:300]}
     if not args.profile and cfg.dtype == gen.BF16:
         try:
             result["clock"] = clock_breakdown(cfg, tile, step, torch, ch, nat)
@@ -263,6 +268,40 @@ def compare_modes(plan, step, stream, cfg, tile, reps, torch, tuning):
         log(tag, {k: v for k, v in out.items() if k.endswith(tag)})
     del scrub
     return out
+
+
+def vendor_gemm_chain(cfg, dX, dW, stream, torch, reps=20):
+    """Context only: the same chain as plain 2-D torch.mm calls (the vendor
+    GEMM library, hipBLASLt), same operands and layout (W stored [K][N]),
+    bf16 in and out, activation between the layers as in the chain; warm,
+    back-to-back runs timed on the stream, median over `reps` bursts of 10."""
+    import torch.nn.functional as F
+
+    def chain():
+        h = dX
+        for l, w in enumerate(dW):
+            h = torch.mm(h, w)
+            if cfg.acts[l] == 1:
+                h = F.gelu(h, approximate="tanh")
+        return h
+
+    with torch.cuda.stream(stream):
+        for _ in range(5):
+            chain()
+        ts = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(10):
+                chain()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3 / 10)
+    med = statistics.median(ts)
+    log(f"vendor GEMM chain (torch.mm): {med:.1f} us")
+    return {"median_us": round(med, 1), "tflops": round(cfg.flops / (med * 1e-6) / 1e12, 1),
+            "what": "torch.mm per layer (hipBLASLt), W as [K][N], warm, context only"}
 
 
 def gpu_state():
