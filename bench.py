@@ -190,7 +190,8 @@ def main():
     # allowed to lose the measurement above
     if not args.profile and not args.no_modes and cfg.dtype == gen.BF16:
         try:
-            result["context_vendor_gemm"] = vendor_gemm_chain(cfg, dX, dW, stream, torch)
+            result["context_vendor_gemm"] = vendor_gemm_chain(cfg, dX, dW, stream, torch, args.steps,
+                                                              args.warmup)
         except Exception as e:
             result["context_vendor_gemm"] = {"error": f"{type(e).__name__}: {e}"[:300]}
     if not args.profile and cfg.dtype == gen.BF16:
@@ -270,11 +271,12 @@ def compare_modes(plan, step, stream, cfg, tile, reps, torch, tuning):
     return out
 
 
-def vendor_gemm_chain(cfg, dX, dW, stream, torch, reps=20):
+def vendor_gemm_chain(cfg, dX, dW, stream, torch, steps, warmup):
     """Context only: the same chain as plain 2-D torch.mm calls (the vendor
     GEMM library, hipBLASLt), same operands and layout (W stored [K][N]),
-    bf16 in and out, activation between the layers as in the chain; warm,
-    back-to-back runs timed on the stream, median over `reps` bursts of 10."""
+    bf16 in and out, activation between the layers as in the chain.  Timed
+    like the headline: `warmup` untimed chains, then `steps` back-to-back
+    chains between two events on the stream."""
     import torch.nn.functional as F
 
     def chain():
@@ -286,22 +288,20 @@ def vendor_gemm_chain(cfg, dX, dW, stream, torch, reps=20):
         return h
 
     with torch.cuda.stream(stream):
-        for _ in range(5):
+        for _ in range(warmup):
             chain()
-        ts = []
-        for _ in range(reps):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(10):
-                chain()
-            e1.record(stream)
-            e1.synchronize()
-            ts.append(e0.elapsed_time(e1) * 1e3 / 10)
-    med = statistics.median(ts)
-    log(f"vendor GEMM chain (torch.mm): {med:.1f} us")
-    return {"median_us": round(med, 1), "tflops": round(cfg.flops / (med * 1e-6) / 1e12, 1),
-            "what": "torch.mm per layer (hipBLASLt), W as [K][N], warm, context only"}
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(steps):
+            chain()
+        e1.record(stream)
+        e1.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    log(f"vendor GEMM chain (torch.mm): {us:.1f} us per chain")
+    return {"latency_us": round(us, 1), "tflops": round(cfg.flops / (us * 1e-6) / 1e12, 1),
+            "what": "torch.mm per layer (hipBLASLt), W as [K][N], timed like the headline; context only"}
 
 
 def gpu_state():
