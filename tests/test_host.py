@@ -255,3 +255,30 @@ def test_bench_roofline_bound(key, bound):
         assert achieved == pytest.approx(cfg.flops / 1e-3 / 1e12)
     if key == "c5":
         assert intensity == pytest.approx(253.7, abs=0.5)
+
+
+@pytest.mark.parametrize("case,code", [
+    ("empty M", nat.CP_ERR_SHAPE), ("negative M", nat.CP_ERR_SHAPE), ("zero layers", nat.CP_ERR_INVALID_ARG),
+    ("zero width", nat.CP_ERR_SHAPE), ("row longer than 2^22", nat.CP_ERR_SHAPE)])
+def test_degenerate_shapes_rejected(case, code):
+    """Empty and degenerate chains are refused with the documented codes,
+    by the host-only graph builder and by the planner before any device
+    work; nothing is launched for them."""
+    M, widths = {"empty M": (0, [512, 512]), "negative M": (-64, [512, 512]),
+                 "zero layers": (128, [512]), "zero width": (128, [512, 0]),
+                 "row longer than 2^22": (128, [1 << 23, 512])}[case]
+    with pytest.raises(nat.CpError) as e:
+        nat.cp_chain_tile_graph(M, widths, 64, 64)
+    assert e.value.code == code
+    with pytest.raises(nat.CpError) as e:
+        nat.cp_chain_plan(M, widths, nat.CP_BF16, 64, 64)
+    assert e.value.code == code
+
+
+def test_null_handles_rejected():
+    """Calls on a NULL plan return CP_ERR_INVALID_ARG (destroy is a no-op)."""
+    for call in (lambda: nat.cp_chain_run(None, 0, [0], 0, None, nat.CP_MODE_PIPELINED),
+                 lambda: nat.cp_chain_stats(None), lambda: nat.cp_chain_trace(None, 4)):
+        with pytest.raises(nat.CpError) as e:
+            call()
+        assert e.value.code == nat.CP_ERR_INVALID_ARG
