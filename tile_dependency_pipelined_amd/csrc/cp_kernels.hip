@@ -31,6 +31,7 @@ namespace cp {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
@@ -104,13 +105,19 @@ constexpr int kRsrcWord3 = 0x00020000;
 // stage that is no longer read, which keeps the number of loads in flight,
 // and so the wait, constant.
 // ----------------------------------------------------------------------------
-template <int BM_, int BN_, int S_, int WGM_ = 2, int WGN_ = 2, int BK_ = 64>
+template <int BM_, int BN_, int S_, int WGM_ = 2, int WGN_ = 2, int BK_ = 64, int MI_ = 32>
 struct Bf16Body {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, S = S_;
     static constexpr int WGM = WGM_, WGN = WGN_;     // wave grid
     static constexpr int NW = WGM * WGN, NT = 64 * NW;
     static constexpr int WM = BM / WGM, WN = BN / WGN;  // per-wave sub-tile
-    static constexpr int FM = WM / 32, FN = WN / 32; // 32x32 MFMA blocks per wave
+    // MFMA block: MI = 32 is v_mfma_f32_32x32x16_bf16 (16 k per step, 16
+    // accumulators per lane), MI = 16 is v_mfma_f32_16x16x32_bf16 (32 k per
+    // step, 4 accumulators per lane: half the accumulator traffic per flop)
+    static constexpr int MI = MI_;
+    static constexpr int KM = MI == 32 ? 16 : 32;    // k per MFMA step
+    static constexpr int ACC = MI * MI / 64;         // fp32 accumulators per lane per block
+    static constexpr int FM = WM / MI, FN = WN / MI; // MFMA blocks per wave
     static constexpr int RB = BN * 2;                // bytes per W row in LDS
     static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * RB;
     static constexpr int A_PW = A_BYTES / 1024 / NW;  // 1 KiB direct loads per wave (A)
@@ -118,6 +125,7 @@ struct Bf16Body {
     static constexpr int PER = A_PW + B_PW;          // loads per wave per slab
     static constexpr int STAGE = A_BYTES + B_BYTES;  // bytes of one LDS stage
     static_assert(BM >= 64 && BN >= 64 && BM <= 256 && BN <= 256, "tile");
+    static_assert(MI == 32 || MI == 16, "MFMA block");
     static_assert(WM >= 32 && WN >= 32 && WM % 32 == 0 && WN % 32 == 0, "wave sub-tile");
     static_assert(A_PW >= 1 && B_PW >= 1 && A_PW * NW * 1024 == A_BYTES && B_PW * NW * 1024 == B_BYTES,
                   "loads per wave");
@@ -132,9 +140,16 @@ struct Bf16Body {
             return L * 128 + ((((r & 1) << 2 | c) ^ ((L ^ (L >> 2)) & 3)) << 4);
         }
     }
+    // W swizzle.  The 16x16x32 B fragment reads rows k, k+8, k+16, k+24 (+0..3)
+    // in one instruction, so there bit 3 of k also moves the chunk.
     __device__ static int fb(int k) {
-        if constexpr (BN >= 128) return (0xCA60 >> ((k & 3) * 4)) & 15;  // 0, 6, 10, 12
-        else return (k & 3) << 1;
+        if constexpr (MI == 32) {
+            if constexpr (BN >= 128) return (0xCA60 >> ((k & 3) * 4)) & 15;  // 0, 6, 10, 12
+            else return (k & 3) << 1;
+        } else {
+            if constexpr (BN >= 128) return ((0xCA60 >> ((k & 3) * 4)) & 15) ^ (((k >> 3) & 1) << 1);
+            else return ((k & 3) << 1) ^ ((k >> 3) & 1);  // stays below 8 chunks
+        }
     }
 
     // `before_epilogue` runs in every thread once the main loop is done (the
@@ -164,13 +179,14 @@ struct Bf16Body {
         const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
         const int wm = wave / WGN, wn = wave % WGN;
 
-        f32x16_t acc[FM][FN];
+        using AccT = std::conditional_t<MI == 32, f32x16_t, f32x4_t>;
+        AccT acc[FM][FN];
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[fm][fn][r] = 0.0f;
+                for (int r = 0; r < ACC; ++r) acc[fm][fn][r] = 0.0f;
 
         // per-lane source offsets (elements) of this wave's direct loads
         // Direct loads are buffer loads: a wave-uniform buffer resource (in
@@ -227,25 +243,35 @@ struct Bf16Body {
         };
 
         // fragment addresses that do not depend on the stage or k step
-        const int g = lane >> 5;                  // k half of the fragment
+        // MI = 32: lanes 32..63 hold the second 8 k of a 16-k step, and a
+        // transpose group of 16 lanes covers 16 of a block's 32 columns.
+        // MI = 16: lane group lane/16 holds k 8 (lane/16) .. +7 of a 32-k step,
+        // and a transpose group covers the block's 16 columns.
+        const int g = MI == 32 ? lane >> 5 : lane >> 4;  // k group of the fragment
         const int s4 = (lane & 15) >> 2;          // row within a transpose group
-        const int nb = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        const int nb = MI == 32 ? 16 * ((lane >> 4) & 1) + 4 * (lane & 3) : 4 * (lane & 3);
         // fragments of one k step (16 k) of the wave's sub-tile
         struct Frags {
             bf16x8_t a[FM], b[FN];
         };
         auto load = [&](const char *As, int kk, Frags &f) {
             const char *Bs = As + A_BYTES;
-            const int c = kk * 2 + g;
+            const int c = kk * (KM / 8) + g;       // 16-byte chunk of the A row
+            auto load_a = [&] {
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const int r = wm * WM + fm * 32 + (lane & 31);
-                f.a[fm] = *reinterpret_cast<const bf16x8_t *>(As + a_at(r, c));
-            }
+                for (int fm = 0; fm < FM; ++fm) {
+                    const int r = wm * WM + fm * MI + (lane & (MI - 1));
+                    f.a[fm] = *reinterpret_cast<const bf16x8_t *>(As + a_at(r, c));
+                }
+            };
+            // MI = 16 reads W first: the A fragments of the next step then
+            // land in the registers of the current step's A fragments, each
+            // read once that fragment's MFMAs are issued
+            if constexpr (MI == 32) load_a();
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
-                const int n = wn * WN + fn * 32 + nb;
-                const int k = kk * 16 + 8 * g + s4;
+                const int n = wn * WN + fn * MI + nb;
+                const int k = kk * KM + 8 * g + s4;
                 const int cn = n >> 3, half = ((n >> 2) & 1) * 8;
                 const char *p0 = Bs + k * RB + ((cn ^ fb(k)) << 4) + half;
                 const char *p1 = Bs + (k + 4) * RB + ((cn ^ fb(k + 4)) << 4) + half;
@@ -254,16 +280,21 @@ struct Bf16Body {
                 const v4i16_t both[2] = {lo, hi};
                 f.b[fn] = *reinterpret_cast<const bf16x8_t *>(both);
             }
+            if constexpr (MI == 16) load_a();
         };
         // W fragment as the first operand: the result holds, per lane, output
-        // row m = lane%32 and four consecutive output columns.
+        // row m = lane mod MI and four consecutive output columns.
         auto mma = [&](const Frags &f) {
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn)
-                    acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[fn], f.a[fm], acc[fm][fn],
-                                                                          0, 0, 0);
+                    if constexpr (MI == 32)
+                        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[fn], f.a[fm], acc[fm][fn],
+                                                                              0, 0, 0);
+                    else
+                        acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.b[fn], f.a[fm], acc[fm][fn],
+                                                                              0, 0, 0);
         };
         // Software pipeline over k steps that crosses slab boundaries: the
         // fragment reads of k step kk+1 are issued between the MFMAs of k step
@@ -274,9 +305,10 @@ struct Bf16Body {
         // refilled, and the next slab has landed.  The scheduling barriers pin
         // the interleaving (the compiler would otherwise group each step's
         // reads right before its own MFMAs).
-        constexpr int KS = BK / 16;                // k steps per slab
+        constexpr int KS = BK / KM;                // k steps per slab
         constexpr int RD = FM + 2 * FN;            // LDS reads per k step
         constexpr int MF = FM * FN;                // MFMAs per k step
+        constexpr bool TWO_PER_READ = MI == 16 && MF == 2 * RD;
         static_assert(KS % 2 == 0, "fragment double buffer parity");
         Frags f[2];
         auto head = [&](const char *As) {          // k steps 0 .. KS-2 of a slab
@@ -288,13 +320,23 @@ struct Bf16Body {
             constexpr int PAIRS = RD < MF ? RD : MF;
 #pragma unroll
             for (int kk = 0; kk + 1 < KS; ++kk) {
+                if constexpr (TWO_PER_READ) {
+                    // two MFMAs per read: the next step's A fragment fm is
+                    // read after the last MFMA of this step's fragment fm
 #pragma unroll
-                for (int r = 0; r < PAIRS; ++r) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one read of step kk+1
+                    for (int r = 0; r < RD; ++r) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one read of step kk+1
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < PAIRS; ++r) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one read of step kk+1
+                    }
+                    if constexpr (RD > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, RD - PAIRS, 0);
+                    if constexpr (MF > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, MF - PAIRS, 0);
                 }
-                if constexpr (RD > PAIRS) __builtin_amdgcn_sched_group_barrier(0x100, RD - PAIRS, 0);
-                if constexpr (MF > PAIRS) __builtin_amdgcn_sched_group_barrier(0x008, MF - PAIRS, 0);
             }
         };
         // last k step of a slab, the refill of its stage and the first reads
@@ -303,12 +345,22 @@ struct Bf16Body {
             issue(refill, k0);
             load(Anext, 0, f[0]);
             mma(f[(KS - 1) & 1]);
-            constexpr int R = MF > RD ? (MF > PER ? MF : PER) : (RD > PER ? RD : PER);
+            if constexpr (TWO_PER_READ) {
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                if (r < MF) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                if (r < RD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                if (r < PER) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                for (int r = 0; r < RD; ++r) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    if (r % 2 == 0 && r / 2 < PER) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                }
+                if constexpr (PER > RD / 2) __builtin_amdgcn_sched_group_barrier(0x020, PER - RD / 2, 0);
+            } else {
+                constexpr int R = MF > RD ? (MF > PER ? MF : PER) : (RD > PER ? RD : PER);
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    if (r < MF) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (r < RD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    if (r < PER) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                }
             }
         };
 
@@ -348,6 +400,7 @@ struct Bf16Body {
 
         if (SPLIT && dp->nsplit > 1) {
             // Partial tile, fragment-native layout [wave][fm][fn][h][lane][2]
+            // (h < ACC / 2)
             // floats: every 8-byte store instruction writes 512 contiguous
             // bytes.  Stored at agent scope (write-through of this XCD's L2);
             // each wave waits for its stores before the barrier, so all of
@@ -359,10 +412,10 @@ struct Bf16Body {
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-                    for (int h = 0; h < 8; ++h) {
+                    for (int h = 0; h < ACC / 2; ++h) {
                         const uint64_t v = (uint64_t)__float_as_uint(acc[fm][fn][2 * h]) |
                                            ((uint64_t)__float_as_uint(acc[fm][fn][2 * h + 1]) << 32);
-                        float *dst = ws + ((((wave * FM + fm) * FN + fn) * 8 + h) * 64 + lane) * 2;
+                        float *dst = ws + ((((wave * FM + fm) * FN + fn) * (ACC / 2) + h) * 64 + lane) * 2;
                         __hip_atomic_store(reinterpret_cast<uint64_t *>(dst), v, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
                     }
@@ -390,15 +443,15 @@ struct Bf16Body {
             for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn) {
-                    const size_t o = ((((size_t)wave * FM + fm) * FN + fn) * 8) * 128 + lane * 2;
-                    f32x16_t sum;
+                    const size_t o = ((((size_t)wave * FM + fm) * FN + fn) * (ACC / 2)) * 128 + lane * 2;
+                    AccT sum;
                     for (int k0 = 0; k0 < ns; k0 += G) {
-                        uint64_t v[G][8];
+                        uint64_t v[G][ACC / 2];
 #pragma unroll
                         for (int g = 0; g < G; ++g) {
                             const int k = k0 + g < ns ? k0 + g : ns - 1;  // in range; unused past ns
 #pragma unroll
-                            for (int h = 0; h < 8; ++h)
+                            for (int h = 0; h < ACC / 2; ++h)
                                 v[g][h] = __hip_atomic_load(
                                     reinterpret_cast<const uint64_t *>(ws0 + (size_t)k * (BM * BN) + o + h * 128),
                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -407,7 +460,7 @@ struct Bf16Body {
                         for (int g = 0; g < G; ++g) {
                             if (k0 + g >= ns) break;
 #pragma unroll
-                            for (int h = 0; h < 8; ++h) {
+                            for (int h = 0; h < ACC / 2; ++h) {
                                 const float v0 = __uint_as_float((uint32_t)v[g][h]);
                                 const float v1 = __uint_as_float((uint32_t)(v[g][h] >> 32));
                                 sum[2 * h] = k0 + g == 0 ? v0 : sum[2 * h] + v0;
@@ -441,19 +494,24 @@ struct Bf16Body {
             return p;
         };
         const int act = dp->act;
-        const int h8 = (lane >> 5) * 8;            // byte half of a 16-byte chunk
+        // A lane holds, per block, output row m = lane mod MI and groups of
+        // four consecutive columns: MI = 32, column 8 gq + 4 (lane / 32) of
+        // the block for accumulators 4 gq .. 4 gq + 3; MI = 16, column
+        // 4 (lane / 16) for its four accumulators.
+        const int h8 = MI == 32 ? (lane >> 5) * 8 : ((lane >> 4) & 1) * 8;  // byte half of a chunk
+        const int cl = MI == 32 ? 0 : (lane >> 5);                       // chunk within the block
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
-            const int rb = wm * WM + fm * 32;      // first row of this fragment block (uniform)
-            const int r = rb + (lane & 31);
+            const int rb = wm * WM + fm * MI;      // first row of this fragment block (uniform)
+            const int r = rb + (lane & (MI - 1));
             char *rowp = stage_of(rb / RPS) + (r % RPS) * (BN * 2) + h8;
             const int key = r % CPR;
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) {
-                const int c0 = (wn * WN + fn * 32) / 8;
-                const f32x16_t &v = acc[fm][fn];
+                const int c0 = (wn * WN + fn * MI) / 8 + cl;
+                const AccT &v = acc[fm][fn];
 #pragma unroll
-                for (int gq = 0; gq < 4; ++gq) {
+                for (int gq = 0; gq < ACC / 4; ++gq) {
                     const uint32_t b0 = f32_to_bf16_rne(act_apply(v[4 * gq + 0], act));
                     const uint32_t b1 = f32_to_bf16_rne(act_apply(v[4 * gq + 1], act));
                     const uint32_t b2 = f32_to_bf16_rne(act_apply(v[4 * gq + 2], act));
@@ -1134,7 +1192,21 @@ hipError_t occupancy_t(int *blocks) {
 #define CP_K_64x64 64
 #endif
 
-#define CP_BODY(bm, bn) Bf16Body<bm, bn, CP_S_##bm##x##bn, CP_W_##bm##x##bn, CP_K_##bm##x##bn>
+// MFMA block per tile shape (32: 32x32x16, 16: 16x16x32)
+#ifndef CP_MI_256x256
+#define CP_MI_256x256 16
+#endif
+#define CP_MI_256x128 32
+#define CP_MI_128x256 32
+#define CP_MI_128x128 32
+#define CP_MI_256x64 32
+#define CP_MI_64x256 32
+#define CP_MI_128x64 32
+#define CP_MI_64x128 32
+#define CP_MI_64x64 32
+
+#define CP_BODY(bm, bn) \
+    Bf16Body<bm, bn, CP_S_##bm##x##bn, CP_W_##bm##x##bn, CP_K_##bm##x##bn, CP_MI_##bm##x##bn>
 #define CP_BF16_VARIANT(bm, bn)                                                                  \
     {CP_BF16, bm, bn, CP_K_##bm##x##bn, CP_S_##bm##x##bn * CP_BODY(bm, bn)::STAGE,                            \
      launch_worker_t<CP_BODY(bm, bn)>, launch_layer_t<CP_BODY(bm, bn)>, occupancy_t<CP_BODY(bm, bn)>}
