@@ -1196,14 +1196,30 @@ hipError_t occupancy_t(int *blocks) {
 #ifndef CP_MI_256x256
 #define CP_MI_256x256 16
 #endif
+#ifndef CP_MI_256x128
 #define CP_MI_256x128 32
+#endif
+#ifndef CP_MI_128x256
 #define CP_MI_128x256 32
+#endif
+#ifndef CP_MI_128x128
 #define CP_MI_128x128 32
+#endif
+#ifndef CP_MI_256x64
 #define CP_MI_256x64 32
+#endif
+#ifndef CP_MI_64x256
 #define CP_MI_64x256 32
+#endif
+#ifndef CP_MI_128x64
 #define CP_MI_128x64 32
+#endif
+#ifndef CP_MI_64x128
 #define CP_MI_64x128 32
+#endif
+#ifndef CP_MI_64x64
 #define CP_MI_64x64 32
+#endif
 
 #define CP_BODY(bm, bn) \
     Bf16Body<bm, bn, CP_S_##bm##x##bn, CP_W_##bm##x##bn, CP_K_##bm##x##bn, CP_MI_##bm##x##bn>
