@@ -140,7 +140,8 @@ typedef struct cp_chain_stats_t {
  *   M         rows of X (the "input sequence length", §IV-A); M % tile_m == 0
  *   n_layers  L, 1 <= L <= CP_MAX_LAYERS
  *   widths    L+1 entries K0, N1, ..., NL; every N_l % tile_n == 0, and every
- *             contraction length K_{l-1} a multiple of 64 (bf16) or 32 (fp32)
+ *             contraction length K_{l-1} a multiple of the tile's k step: 64
+ *             for bf16 (128 for 256 x 256 tiles), 32 for fp32
  *   dtype     CP_F32 or CP_BF16
  *   tile_m,n  output tile of one workgroup (one CTA, §III).  bf16: each of
  *             64, 128, 256; fp32: 64 x 64.  Other tiles: CP_ERR_UNSUPPORTED.

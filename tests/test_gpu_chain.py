@@ -133,9 +133,12 @@ BF16_TILES = [(256, 256), (256, 128), (128, 256), (128, 128), (256, 64), (64, 25
 def test_bf16_small_parity(rt, tile):
     bm, bn = tile
     M = 3 * bm
-    widths = (320, 3 * bn, 2 * bn)
+    # an odd number of 64-k slabs exercises the k loop's remainder step; the
+    # 256x256 body takes k in steps of 128 (two slabs) and has none
+    k0 = 384 if tile == (256, 256) else 320
+    widths = (k0, 3 * bn, 2 * bn)
     say("bf16 small", tile, M, widths)
-    X, Ws = gen.chain_inputs(M, widths, gen.BF16, 1.0, (1 / np.sqrt(320), 1 / np.sqrt(3 * bn)), 50)
+    X, Ws = gen.chain_inputs(M, widths, gen.BF16, 1.0, (1 / np.sqrt(k0), 1 / np.sqrt(3 * bn)), 50)
     out, st = run_modes(rt, X, Ws, gen.BF16, tile, flags=all_flags(),
                         modes=("pipelined", "sequential", "microbatch", "spatial"), mb_rows=bm)
     ref = oracle.chain(X, Ws, gen.BF16)

@@ -207,9 +207,12 @@ def test_error_codes_without_device():
     with pytest.raises(nat.CpError) as e:
         nat.cp_chain_plan(128, [512, 512], nat.CP_F32, 128, 128)
     assert e.value.code == nat.CP_ERR_UNSUPPORTED
-    # k not a multiple of the k step
+    # k not a multiple of the k step (64 for bf16; 128 for 256x256 tiles)
     with pytest.raises(nat.CpError) as e:
         nat.cp_chain_plan(128, [96, 512], nat.CP_BF16, 64, 64)
+    assert e.value.code == nat.CP_ERR_SHAPE
+    with pytest.raises(nat.CpError) as e:
+        nat.cp_chain_plan(256, [320, 256], nat.CP_BF16, 256, 256)
     assert e.value.code == nat.CP_ERR_SHAPE
     with pytest.raises(nat.CpError) as e:
         nat.cp_chain_plan(128, [512, 512], 7, 64, 64)

@@ -118,6 +118,11 @@ struct Bf16Body {
     static constexpr int KM = MI == 32 ? 16 : 32;    // k per MFMA step
     static constexpr int ACC = MI * MI / 64;         // fp32 accumulators per lane per block
     static constexpr int FM = WM / MI, FN = WN / MI; // MFMA blocks per wave
+    // k granularity the plan guarantees per item (its k step): one slab, or
+    // for the 16x16x32 body S slabs, so that its k loop needs no remainder
+    // step (a remainder keeps the loop's addresses live past it, which the
+    // persistent worker of that body can only afford by spilling them)
+    static constexpr int KQ = MI == 16 ? BK * S : BK;
     static constexpr int RB = BN * 2;                // bytes per W row in LDS
     static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BK * RB;
     static constexpr int A_PW = A_BYTES / 1024 / NW;  // 1 KiB direct loads per wave (A)
@@ -389,10 +394,12 @@ struct Bf16Body {
             if constexpr (S > 3) step(ic<3 % S>{}, slab + 3);
             if constexpr (S > 4) step(ic<4 % S>{}, slab + 4);
         }
-        if (slab < nk) step(ic<0>{}, slab++);
-        if constexpr (S > 2) if (slab < nk) step(ic<1 % S>{}, slab++);
-        if constexpr (S > 3) if (slab < nk) step(ic<2 % S>{}, slab++);
-        if constexpr (S > 4) if (slab < nk) step(ic<3 % S>{}, slab++);
+        if constexpr (KQ % (BK * S) != 0) {
+            if (slab < nk) step(ic<0>{}, slab++);
+            if constexpr (S > 2) if (slab < nk) step(ic<1 % S>{}, slab++);
+            if constexpr (S > 3) if (slab < nk) step(ic<2 % S>{}, slab++);
+            if constexpr (S > 4) if (slab < nk) step(ic<3 % S>{}, slab++);
+        }
         wait_vmcnt<0>();  // the trailing prefetches must land before the LDS is reused
         __syncthreads();
         before_epilogue();
@@ -951,7 +958,11 @@ __device__ __forceinline__ void decode(const ChainArgs &a, uint32_t id, int &l, 
 __device__ void reset_copy(const ChainArgs &a, uint32_t *queue, uint32_t *ctl, int32_t *score,
                            uint32_t *deq_count, uint64_t *trace, uint32_t *arrive) {
     const int stride = gridDim.x * blockDim.x;
-    for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < a.T; t += stride) {
+    // opaque thread index: a persistent worker calls this on its way out,
+    // and nothing of it should be computed early and held across its tiles
+    int tx = threadIdx.x;
+    __asm__ volatile("" : "+v"(tx));
+    for (int t = blockIdx.x * blockDim.x + tx; t < a.T; t += stride) {
         score[t] = a.indeg[t];
         queue[t] = a.qinit[t];
         arrive[t] = 0;
@@ -959,8 +970,8 @@ __device__ void reset_copy(const ChainArgs &a, uint32_t *queue, uint32_t *ctl, i
         if (trace)
             for (int w = 0; w < kTraceWords; ++w) trace[kTraceWords * (size_t)t + w] = 0;
     }
-    if (blockIdx.x == 0 && threadIdx.x < kMaxQueues) {
-        const int q = threadIdx.x;
+    if (blockIdx.x == 0 && tx < kMaxQueues) {
+        const int q = tx;
         // slots 0 .. (workers of queue q) - 1 are handed out statically
         ctl[ctl_head(q)] = q < a.nq ? (uint32_t)a.qworkers[q] : 0u;
         ctl[ctl_tail(q)] = q < a.nq ? (uint32_t)a.qfirst[q] : 0u;
@@ -1224,7 +1235,7 @@ hipError_t occupancy_t(int *blocks) {
 #define CP_BODY(bm, bn) \
     Bf16Body<bm, bn, CP_S_##bm##x##bn, CP_W_##bm##x##bn, CP_K_##bm##x##bn, CP_MI_##bm##x##bn>
 #define CP_BF16_VARIANT(bm, bn)                                                                  \
-    {CP_BF16, bm, bn, CP_K_##bm##x##bn, CP_S_##bm##x##bn * CP_BODY(bm, bn)::STAGE,                            \
+    {CP_BF16, bm, bn, CP_BODY(bm, bn)::KQ, CP_S_##bm##x##bn * CP_BODY(bm, bn)::STAGE,                         \
      launch_worker_t<CP_BODY(bm, bn)>, launch_layer_t<CP_BODY(bm, bn)>, occupancy_t<CP_BODY(bm, bn)>}
 
 static const Variant kVariants[] = {
