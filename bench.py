@@ -182,7 +182,14 @@ def main():
     }
 
     if not args.no_modes and not args.profile:
-        result["modes"] = compare_modes(plan, step, stream, cfg, tile, args.reps, torch, tuning)
+        # spatial runs get a plan of their own: a plan's two per-run state
+        # copies are laid out for one queue layout at a time, and a pipelined
+        # run after a spatial run on the same plan would first re-lay one
+        # out (an extra reset launch inside its timed span)
+        with ch.Chain(cfg.M, cfg.widths, cfg.dtype, tile[0], tile[1], acts=list(cfg.acts)) as sp:
+            def step_modes(mode="pipelined", mb=0):
+                step(mode, mb, p=sp if mode == "spatial" else plan)
+            result["modes"] = compare_modes(plan, step_modes, stream, cfg, tile, args.reps, torch, tuning)
 
     if not args.profile:
         result["gpu_state_after_timed_steps"] = gpu_state()
@@ -224,9 +231,10 @@ def roofline(flops, min_bytes, launch_ms, peak_tflops):
 def compare_modes(plan, step, stream, cfg, tile, reps, torch, tuning):
     """Latency of single runs of each mode, warm (back to back) and cold (a
     1 GiB device write before each run, outside the timed span).  The modes
-    are interleaved, one run of each per round, so that clock and thermal
-    drift affect them alike; a short GPU sleep before the start event keeps
-    host submission time out of the span.  Median, min, p10, p90 per mode."""
+    are interleaved, one run of each per round in a rotating order, so that
+    clock and thermal drift and the previous run's cache contents affect them
+    alike; a short GPU sleep before the start event keeps host submission
+    time out of the span.  Median, min, p10, p90 per mode."""
     scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
     runs = [("pipelined", 0), ("sequential", 0), ("spatial", 0)]
     runs += [("microbatch", m) for m in tuning.chunk_sweep(cfg.M, tile[0])]
@@ -255,8 +263,12 @@ def compare_modes(plan, step, stream, cfg, tile, reps, torch, tuning):
     for cold in (False, True):
         tag = "cold" if cold else "warm"
         ts = {r: [] for r in runs}
-        for _ in range(reps):
-            for r in runs:
+        # the starting mode rotates from round to round, so that every mode
+        # follows every other one equally often (what ran just before leaves
+        # its lines in the caches and its clock state behind)
+        for rep in range(reps):
+            k = rep % len(runs)
+            for r in runs[k:] + runs[:k]:
                 ts[r].append(one(r[0], r[1], cold))
         for name in ("pipelined", "sequential", "spatial"):
             out[f"{name}_{tag}"] = summary(ts[(name, 0)])
