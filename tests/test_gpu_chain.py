@@ -321,6 +321,23 @@ def test_split_k_layers(rt, acts):
     assert oracle.rel_err(as_values(out2["pipelined"], gen.BF16), ref) <= TOL[gen.BF16]
 
 
+def test_split_k_256_tiles(rt):
+    """Split-K with the 256x256 body (16x16x32 blocks, k step 128): a
+    two-tile first layer with k = 8192 is split four ways; every mode gives
+    the same bits and the result matches the oracle."""
+    M, widths = 256, (8192, 512, 256)
+    X, Ws = gen.chain_inputs(M, widths, gen.BF16, 1.0, (1 / np.sqrt(8192), 1 / np.sqrt(512)), 89)
+    say("split-K chain, 256x256 tiles", M, widths)
+    out, st = run_modes(rt, X, Ws, gen.BF16, (256, 256), acts=[gen.ACT_GELU_TANH, gen.ACT_NONE],
+                        flags=all_flags(), modes=("pipelined", "sequential", "spatial"), reps=2)
+    say("nsplit", st["nsplit"], "items", st["n_tiles"])
+    assert st["nsplit"][0] > 1, st["nsplit"]
+    ref = oracle.chain(X, Ws, gen.BF16, acts=[gen.ACT_GELU_TANH, gen.ACT_NONE])
+    assert oracle.rel_err(as_values(out["pipelined"], gen.BF16), ref) <= TOL[gen.BF16]
+    for m in ("sequential", "spatial"):
+        assert same_bits(out["pipelined"], out[m]), m
+
+
 def test_split_k_many_partials(rt):
     """A long-k layer with two tiles is split into 16 items per tile, so the
     last item to arrive sums its partials in several groups of loads; the
