@@ -1116,6 +1116,44 @@ hipError_t occupancy_t(int *blocks) {
     return hipSuccess;
 }
 
+// A tile shape whose plain body differs from its split-K body: a plan with
+// any split layer runs every launch (worker and layer kernels, every mode)
+// on the split body, a plan without one on the plain body, so that one plan
+// always computes with one body and its modes agree bit for bit.  Used for
+// 256x256 tiles, whose 16x16x32 body spills heavily in its split-K worker.
+inline bool plan_splits(const ChainArgs &a) {
+    for (int l = 0; l < a.L; ++l)
+        if (a.layer[l].nsplit > 1) return true;
+    return false;
+}
+
+template <class Plain, class Split>
+hipError_t launch_worker_p(const ChainArgs &a, int grid, bool cooperative, hipStream_t s) {
+    if (plan_splits(a)) return launch_worker_s<Split, true>(a, grid, cooperative, s);
+    return launch_worker_s<Plain, false>(a, grid, cooperative, s);
+}
+
+template <class Plain, class Split>
+hipError_t launch_layer_p(const ChainArgs &a, int l, int rb0, int nrb, hipStream_t s) {
+    if (plan_splits(a)) return launch_layer_t<Split>(a, l, rb0, nrb, s);
+    const int grid = nrb * a.layer[l].nbn;
+    if (grid <= 0) return hipSuccess;
+    hipLaunchKernelGGL((layer_kernel<Plain, false>), dim3(grid), dim3(Plain::NT), 0, s, a, l, rb0);
+    return hipGetLastError();
+}
+
+// as occupancy_t, over the two worker instantiations such a shape launches
+template <class Plain, class Split>
+hipError_t occupancy_p(int *blocks) {
+    int plain = 0, split = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&plain, worker_kernel<Plain, false>, Plain::NT, 0);
+    if (e != hipSuccess) return e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&split, worker_kernel<Split, true>, Split::NT, 0);
+    if (e != hipSuccess) return e;
+    *blocks = split < plain ? split : plain;
+    return hipSuccess;
+}
+
 // LDS stages per tile shape: as many as fit the occupancy each shape aims for
 #ifndef CP_S_256x256
 #define CP_S_256x256 2
@@ -1234,6 +1272,12 @@ hipError_t occupancy_t(int *blocks) {
 
 #define CP_BODY(bm, bn) \
     Bf16Body<bm, bn, CP_S_##bm##x##bn, CP_W_##bm##x##bn, CP_K_##bm##x##bn, CP_MI_##bm##x##bn>
+// split-K body of a shape: always the 32x32x16 blocks
+#define CP_SPLIT_BODY(bm, bn) Bf16Body<bm, bn, CP_S_##bm##x##bn, CP_W_##bm##x##bn, CP_K_##bm##x##bn, 32>
+#define CP_BF16_VARIANT_PAIR(bm, bn)                                                             \
+    {CP_BF16, bm, bn, CP_BODY(bm, bn)::KQ, CP_S_##bm##x##bn * CP_BODY(bm, bn)::STAGE,                         \
+     launch_worker_p<CP_BODY(bm, bn), CP_SPLIT_BODY(bm, bn)>,                                          \
+     launch_layer_p<CP_BODY(bm, bn), CP_SPLIT_BODY(bm, bn)>, occupancy_p<CP_BODY(bm, bn), CP_SPLIT_BODY(bm, bn)>}
 #define CP_BF16_VARIANT(bm, bn)                                                                  \
     {CP_BF16, bm, bn, CP_BODY(bm, bn)::KQ, CP_S_##bm##x##bn * CP_BODY(bm, bn)::STAGE,                         \
      launch_worker_t<CP_BODY(bm, bn)>, launch_layer_t<CP_BODY(bm, bn)>, occupancy_t<CP_BODY(bm, bn)>}
@@ -1241,7 +1285,7 @@ hipError_t occupancy_t(int *blocks) {
 static const Variant kVariants[] = {
     {CP_F32, 64, 64, 32, 2 * F32Body::STAGE, launch_worker_t<F32Body>, launch_layer_t<F32Body>,
      occupancy_t<F32Body>},
-    CP_BF16_VARIANT(256, 256), CP_BF16_VARIANT(256, 128), CP_BF16_VARIANT(128, 256),
+    CP_BF16_VARIANT_PAIR(256, 256), CP_BF16_VARIANT(256, 128), CP_BF16_VARIANT(128, 256),
     CP_BF16_VARIANT(128, 128), CP_BF16_VARIANT(256, 64),  CP_BF16_VARIANT(64, 256),
     CP_BF16_VARIANT(128, 64),  CP_BF16_VARIANT(64, 128),  CP_BF16_VARIANT(64, 64),
 };
