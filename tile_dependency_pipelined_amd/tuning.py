@@ -2,10 +2,12 @@
 sizes.  Used by the benchmark and by the parity tests, so that the tests
 check exactly the configuration that is timed."""
 
-# (tile_m, tile_n) per workload key of inputs.CONFIGS
-# chosen by the steady-state pipelined time of each candidate on one MI355X
-# (C2: 128x64 78 us vs 128x128 94 us; C4: 128x128 537 us vs 256x128 548 us;
-# C5: 128x128 and 256x128 both ~572 us)
+# (tile_m, tile_n) per workload key of inputs.CONFIGS, chosen by the
+# pipelined time of each candidate, interleaved on one MI355X (microseconds):
+#   C2: 128x64 64-66; 64x128 69; 64x64 75; 64x256 75; 256x64 80; 128x128 110
+#   C3: 256x256 395-428; 256x128 517; 128x256 521
+#   C4: 128x128 514-524; 256x128 545; 256x256 539 (split 2)
+#   C5: 128x128 303-313; 256x64 376; 64x256 381; 128x256 407; 256x128 416
 TILES = {
     "c1": (64, 64),
     "c2": (128, 64),
