@@ -12,7 +12,8 @@
 // baselines, so all modes produce bit-identical results.
 //
 // gfx950 mapping (MI355X): 4 wave64 per workgroup (8 for 256 x 256 tiles);
-// bf16 tiles use v_mfma_f32_32x32x16_bf16 with fp32 accumulators, fp32 tiles
+// bf16 tiles use fp32-accumulating MFMAs, v_mfma_f32_16x16x32_bf16 for
+// 256 x 256 tiles and v_mfma_f32_32x32x16_bf16 for the others; fp32 tiles
 // v_mfma_f32_32x32x2_f32.  The paper's system-wide threadfence becomes, on
 // one GPU, agent scope: by default the producer writes intermediate tiles
 // with agent-scope (L2 write-through) stores and waits for their completion
@@ -90,7 +91,10 @@ constexpr int kRsrcWord3 = 0x00020000;
 //   W tile [64][BN] bf16 in its natural n-contiguous layout, chunk c of row k
 //     stored at c ^ fb(k), fb = {0, 6, 10, 12}[k mod 4] (BN >= 128): the 4
 //     rows x 2 chunks read by 16 lanes are distinct modulo 128 bytes and the
-//     4 rows x 4 chunks read by 32 lanes distinct modulo 256 bytes.
+//     4 rows x 4 chunks read by 32 lanes distinct modulo 256 bytes.  With
+//     16x16x32 blocks, 32 lanes read rows k .. k+3 and k+8 .. k+11 x 2
+//     chunks; there fb also flips chunk bit 1 with bit 3 of k, which keeps
+//     those 16 chunks distinct modulo 256 bytes.
 //     The B fragment (8 consecutive k of one column)
 //     is read by two ds_read_b64_tr_b16: within a group of 16 lanes, result
 //     lane i, element j is element (i mod 4) of the 8 bytes addressed by lane
