@@ -82,12 +82,18 @@ constexpr int kRsrcWord3 = 0x00020000;
 // store instructions are needed; the swizzle below is applied by choosing
 // which global 16-byte chunk each lane fetches.
 //   A tile [BM][BK] bf16.  BK = 64: 128-byte rows, chunk c of row r stored at
-//     chunk position c ^ fa(r), fa(r) = (r ^ (r >> 3)) & 7.  BK = 32: rows
-//     2L and 2L+1 share the 128-byte line L, chunk c of row r at position
-//     (4 (r & 1) + c) ^ fl(L), fl(L) = (L ^ (L >> 2)) & 3.  Either way the
-//     MFMA A fragment (8 consecutive k of one row) is one ds_read_b128, 8
-//     consecutive rows hit 8 distinct 16-byte bank groups of a 128-byte
-//     window, and 16 consecutive rows 16 distinct groups of a 256-byte window.
+//     chunk position c ^ fa(r).  BK = 32: rows 2L and 2L+1 share the
+//     128-byte line L, chunk c of row r at position (4 (r & 1) + c) ^ fl(L),
+//     fl(L) = (L ^ (L >> 2)) & 3.  The MFMA A fragment (8 consecutive k of
+//     one row) is one ds_read_b128, and a 128-bit LDS read is served in
+//     pairs of 8-lane groups, lanes l .. l+7 with lanes l+32 .. l+39 (these
+//     16 reads must fall on distinct 16-byte bank groups of a 256-byte
+//     window), as well as in plain 16-lane groups.  With 32x32x16 blocks,
+//     lanes l and l+32 read chunks c and c+1 of one row; fa(r) =
+//     (r ^ (r >> 3)) & 7 keeps both groupings conflict-free.  With 16x16x32
+//     blocks they read chunks c and c+2, where that fa collides; there
+//     fa(r) = r1 | r3 << 1 | r2 << 2 (ri = bit i of r) is conflict-free in
+//     both groupings.
 //   W tile [64][BN] bf16 in its natural n-contiguous layout, chunk c of row k
 //     stored at c ^ fb(k), fb = {0, 6, 10, 12}[k mod 4] (BN >= 128): the 4
 //     rows x 2 chunks read by 16 lanes are distinct modulo 128 bytes and the
@@ -141,9 +147,14 @@ struct Bf16Body {
     static_assert(BK == 32 || BK == 64, "k slab");
     static_assert(S >= 2 && S <= 5 && (S - 1) * PER < 64, "stages");
 
+    // A swizzle for BK = 64 (header comment): chunk position of chunk 0 of row r
+    __device__ static int fa(int r) {
+        if constexpr (MI == 32) return (r ^ (r >> 3)) & 7;
+        else return ((r >> 1) & 1) | (((r >> 3) & 1) << 1) | (((r >> 2) & 1) << 2);
+    }
     // byte offset of 16-byte chunk c (0 .. BK/8-1) of A row r within the A tile
     __device__ static int a_at(int r, int c) {
-        if constexpr (BK == 64) return r * 128 + ((c ^ ((r ^ (r >> 3)) & 7)) << 4);
+        if constexpr (BK == 64) return r * 128 + ((c ^ fa(r)) << 4);
         else {
             const int L = r >> 1;
             return L * 128 + ((((r & 1) << 2 | c) ^ ((L ^ (L >> 2)) & 3)) << 4);
@@ -212,7 +223,7 @@ struct Bf16Body {
             int r, c;
             if constexpr (BK == 64) {
                 r = o >> 7;
-                c = ((o >> 4) & 7) ^ ((r ^ (r >> 3)) & 7);
+                c = ((o >> 4) & 7) ^ fa(r);
             } else {  // inverse of a_at for 64-byte rows
                 const int L = o >> 7, v = ((o >> 4) & 7) ^ ((L ^ (L >> 2)) & 3);
                 r = 2 * L + (v >> 2);
