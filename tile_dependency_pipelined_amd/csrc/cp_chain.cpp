@@ -129,8 +129,9 @@ void choose_splits(int64_t M, int32_t L, const int64_t *widths, int32_t tile_m, 
     for (int l = 0; l < L; ++l) {
         ns[l] = 1;
         if (!allow) continue;
-        // an item keeps at least 16 slabs of 64 k (bf16) or 2 slabs of 32 k
-        // (fp32: its small tiles leave most of the device idle otherwise)
+        // an item keeps at least 16 k steps of the tile body (bf16: 64 k, or
+        // 128 k for 256x256 tiles) or 2 steps of 32 k (fp32: its small tiles
+        // leave most of the device idle otherwise)
         const int64_t min_slabs = dtype == CP_BF16 ? 16 : 2;
         const int64_t tiles = nrb * (widths[l + 1] / tile_n), slabs = widths[l] / k_step;
         const int64_t prod_tiles = l > 0 ? widths[l] / tile_n : 0;

@@ -808,6 +808,10 @@ struct Stages<Body, 4> {
 
 // ----------------------------------------------------------------------------
 // Protocol: prologue (consumer side) and publish (producer side).
+// Every helper that takes the kernel's ChainArgs by reference is inlined:
+// an out-of-line call needs the argument's address, and the compiler then
+// copies the whole by-value kernel argument (about 800 bytes) into private
+// memory at kernel start, which also costs the registers it stages through.
 // ----------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t ld_relaxed(const uint32_t *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -831,7 +835,7 @@ __device__ __forceinline__ uint32_t ld_relaxed(const uint32_t *p) {
 // wait lasts forever for a well-formed dependency table; if the device is
 // shared and some workers are not resident, the watchdog ends the run with
 // a timeout.
-__device__ uint32_t take_ticket(const ChainArgs &a, int q) {
+__device__ __forceinline__ uint32_t take_ticket(const ChainArgs &a, int q) {
     if (ld_relaxed(a.ctl + kCtlStatus) != 0) return kDone;  // >= any queue size
     return __hip_atomic_fetch_add(a.ctl + ctl_head(q), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -847,7 +851,7 @@ __device__ __forceinline__ void dequeued(const ChainArgs &a, uint32_t id, uint64
     }
 }
 
-__device__ uint32_t wait_slot(const ChainArgs &a, int q, uint32_t t) {
+__device__ __forceinline__ uint32_t wait_slot(const ChainArgs &a, int q, uint32_t t) {
     if (t >= (uint32_t)a.qsize[q]) return kDone;
     const uint32_t *slot = a.queue + a.qbase[q] + t;
     const uint64_t t0 = wall_clock64();
@@ -882,7 +886,7 @@ __device__ uint32_t wait_slot(const ChainArgs &a, int q, uint32_t t) {
 // A worker's first slot is its own (no ticket atomic) and, for the
 // pre-filled first-layer slots, its content is known: compute it instead
 // of reading it, which saves the first tile a memory round trip.
-__device__ uint32_t first_slot(const ChainArgs &a, int q, uint32_t t) {
+__device__ __forceinline__ uint32_t first_slot(const ChainArgs &a, int q, uint32_t t) {
     if (!a.first_formula || t >= (uint32_t)a.qfirst[q]) return wait_slot(a, q, t);
     const uint64_t t0 = a.trace ? wall_clock64() : 0;
     const uint32_t id = first_item(a.layer[0].nbn * a.layer[0].nsplit, a.nq, q, t);
@@ -901,7 +905,7 @@ __device__ uint32_t first_slot(const ChainArgs &a, int q, uint32_t t) {
 // Wave 0 then decrements the counter of every consumer (all in layer l+1),
 // one edge per lane, and pushes the consumers whose counter reached zero into
 // their owner queues, one tail atomic per queue.
-__device__ void publish(const ChainArgs &a, uint32_t id, int l) {
+__device__ __forceinline__ void publish(const ChainArgs &a, uint32_t id, int l) {
     const bool fenced = (a.flags & CP_FLAG_FENCE_RELEASE) != 0;
     if (!fenced) wait_vmcnt<0>();
     __syncthreads();
@@ -970,7 +974,7 @@ __device__ __forceinline__ void decode(const ChainArgs &a, uint32_t id, int &l, 
 // queues from their initial image (each pre-filled with its first-layer
 // tiles in row-block-major order, EMPTY after), per-queue head = 0,
 // tail = pre-filled, status OK.  Grid-stride over the calling grid.
-__device__ void reset_copy(const ChainArgs &a, uint32_t *queue, uint32_t *ctl, int32_t *score,
+__device__ __forceinline__ void reset_copy(const ChainArgs &a, uint32_t *queue, uint32_t *ctl, int32_t *score,
                            uint32_t *deq_count, uint64_t *trace, uint32_t *arrive) {
     const int stride = gridDim.x * blockDim.x;
     // opaque thread index: a persistent worker calls this on its way out,
@@ -1131,44 +1135,6 @@ hipError_t occupancy_t(int *blocks) {
     return hipSuccess;
 }
 
-// A tile shape whose plain body differs from its split-K body: a plan with
-// any split layer runs every launch (worker and layer kernels, every mode)
-// on the split body, a plan without one on the plain body, so that one plan
-// always computes with one body and its modes agree bit for bit.  Used for
-// 256x256 tiles, whose 16x16x32 body spills heavily in its split-K worker.
-inline bool plan_splits(const ChainArgs &a) {
-    for (int l = 0; l < a.L; ++l)
-        if (a.layer[l].nsplit > 1) return true;
-    return false;
-}
-
-template <class Plain, class Split>
-hipError_t launch_worker_p(const ChainArgs &a, int grid, bool cooperative, hipStream_t s) {
-    if (plan_splits(a)) return launch_worker_s<Split, true>(a, grid, cooperative, s);
-    return launch_worker_s<Plain, false>(a, grid, cooperative, s);
-}
-
-template <class Plain, class Split>
-hipError_t launch_layer_p(const ChainArgs &a, int l, int rb0, int nrb, hipStream_t s) {
-    if (plan_splits(a)) return launch_layer_t<Split>(a, l, rb0, nrb, s);
-    const int grid = nrb * a.layer[l].nbn;
-    if (grid <= 0) return hipSuccess;
-    hipLaunchKernelGGL((layer_kernel<Plain, false>), dim3(grid), dim3(Plain::NT), 0, s, a, l, rb0);
-    return hipGetLastError();
-}
-
-// as occupancy_t, over the two worker instantiations such a shape launches
-template <class Plain, class Split>
-hipError_t occupancy_p(int *blocks) {
-    int plain = 0, split = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&plain, worker_kernel<Plain, false>, Plain::NT, 0);
-    if (e != hipSuccess) return e;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&split, worker_kernel<Split, true>, Split::NT, 0);
-    if (e != hipSuccess) return e;
-    *blocks = split < plain ? split : plain;
-    return hipSuccess;
-}
-
 // LDS stages per tile shape: as many as fit the occupancy each shape aims for
 #ifndef CP_S_256x256
 #define CP_S_256x256 2
@@ -1287,12 +1253,6 @@ hipError_t occupancy_p(int *blocks) {
 
 #define CP_BODY(bm, bn) \
     Bf16Body<bm, bn, CP_S_##bm##x##bn, CP_W_##bm##x##bn, CP_K_##bm##x##bn, CP_MI_##bm##x##bn>
-// split-K body of a shape: always the 32x32x16 blocks
-#define CP_SPLIT_BODY(bm, bn) Bf16Body<bm, bn, CP_S_##bm##x##bn, CP_W_##bm##x##bn, CP_K_##bm##x##bn, 32>
-#define CP_BF16_VARIANT_PAIR(bm, bn)                                                             \
-    {CP_BF16, bm, bn, CP_BODY(bm, bn)::KQ, CP_S_##bm##x##bn * CP_BODY(bm, bn)::STAGE,                         \
-     launch_worker_p<CP_BODY(bm, bn), CP_SPLIT_BODY(bm, bn)>,                                          \
-     launch_layer_p<CP_BODY(bm, bn), CP_SPLIT_BODY(bm, bn)>, occupancy_p<CP_BODY(bm, bn), CP_SPLIT_BODY(bm, bn)>}
 #define CP_BF16_VARIANT(bm, bn)                                                                  \
     {CP_BF16, bm, bn, CP_BODY(bm, bn)::KQ, CP_S_##bm##x##bn * CP_BODY(bm, bn)::STAGE,                         \
      launch_worker_t<CP_BODY(bm, bn)>, launch_layer_t<CP_BODY(bm, bn)>, occupancy_t<CP_BODY(bm, bn)>}
@@ -1300,7 +1260,7 @@ hipError_t occupancy_p(int *blocks) {
 static const Variant kVariants[] = {
     {CP_F32, 64, 64, 32, 2 * F32Body::STAGE, launch_worker_t<F32Body>, launch_layer_t<F32Body>,
      occupancy_t<F32Body>},
-    CP_BF16_VARIANT_PAIR(256, 256), CP_BF16_VARIANT(256, 128), CP_BF16_VARIANT(128, 256),
+    CP_BF16_VARIANT(256, 256), CP_BF16_VARIANT(256, 128), CP_BF16_VARIANT(128, 256),
     CP_BF16_VARIANT(128, 128), CP_BF16_VARIANT(256, 64),  CP_BF16_VARIANT(64, 256),
     CP_BF16_VARIANT(128, 64),  CP_BF16_VARIANT(64, 128),  CP_BF16_VARIANT(64, 64),
 };
