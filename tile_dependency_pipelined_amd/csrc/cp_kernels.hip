@@ -453,45 +453,97 @@ struct Bf16Body {
             // Last to arrive: every item's partial, this one's included, is in
             // memory.  Reset the count for the next run and sum the partials in
             // split order (the same order whichever item arrives last), reading
-            // them at agent scope so that no cached line can be stale.  The
-            // loads of up to four partials of one 32x32 block are all issued
-            // before any of them is used: one memory round trip per block and
-            // group of four, instead of one per partial and 8-byte pair.
+            // them at agent scope so that no cached line can be stale.  With
+            // more than four partials the loads of up to four partials of one
+            // block are all issued before any of them is used: one memory
+            // round trip per block and group of four, instead of one per
+            // partial and 8-byte pair.
             if (tid == 0) __hip_atomic_store(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             const float *ws0 = dp->ws + (size_t)(tile * dp->nsplit) * (BM * BN);
             const int ns = dp->nsplit;
             constexpr int G = 4;                   // partials loaded per group
+            auto part = [&](int k, int fm, int fn, int h) -> uint64_t {
+                const size_t o = ((((size_t)wave * FM + fm) * FN + fn) * (ACC / 2)) * 128 + lane * 2;
+                return __hip_atomic_load(
+                    reinterpret_cast<const uint64_t *>(ws0 + (size_t)k * (BM * BN) + o + h * 128),
+                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            };
+            // Two or four partials (the common splits): the reduction runs
+            // over units of HC 8-byte pairs of one block, and the loads of the
+            // next unit are issued before the current one is summed, so the
+            // wave waits for about one memory round trip in all rather than
+            // one per block.  Two units of loads in flight hold 64 VGPRs, as
+            // the one group of the general loop below does.
+            auto reduce_pipelined = [&](auto nsc) {
+                constexpr int NS = decltype(nsc)::value;
+                constexpr int HC = 16 / NS < ACC / 2 ? 16 / NS : ACC / 2;
+                constexpr int UPB = (ACC / 2) / HC;  // units per block
+                constexpr int NU = FM * FN * UPB;
+                uint64_t v[2][NS][HC];
+                auto issue_unit = [&](int u, uint64_t (&dst)[NS][HC]) {
+                    const int blk = u / UPB, h0 = (u % UPB) * HC;
 #pragma unroll
-            for (int fm = 0; fm < FM; ++fm)
+                    for (int k = 0; k < NS; ++k)
 #pragma unroll
-                for (int fn = 0; fn < FN; ++fn) {
-                    const size_t o = ((((size_t)wave * FM + fm) * FN + fn) * (ACC / 2)) * 128 + lane * 2;
-                    AccT sum;
-                    for (int k0 = 0; k0 < ns; k0 += G) {
-                        uint64_t v[G][ACC / 2];
+                        for (int h = 0; h < HC; ++h) dst[k][h] = part(k, blk / FN, blk % FN, h0 + h);
+                };
+                issue_unit(0, v[0]);
 #pragma unroll
-                        for (int g = 0; g < G; ++g) {
-                            const int k = k0 + g < ns ? k0 + g : ns - 1;  // in range; unused past ns
+                for (int u = 0; u < NU; ++u) {
+                    if (u + 1 < NU) issue_unit(u + 1, v[(u + 1) & 1]);
+                    const int blk = u / UPB, h0 = (u % UPB) * HC;
 #pragma unroll
-                            for (int h = 0; h < ACC / 2; ++h)
-                                v[g][h] = __hip_atomic_load(
-                                    reinterpret_cast<const uint64_t *>(ws0 + (size_t)k * (BM * BN) + o + h * 128),
-                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    for (int h = 0; h < HC; ++h) {
+                        float s0 = __uint_as_float((uint32_t)v[u & 1][0][h]);
+                        float s1 = __uint_as_float((uint32_t)(v[u & 1][0][h] >> 32));
+#pragma unroll
+                        for (int k = 1; k < NS; ++k) {
+                            s0 = s0 + __uint_as_float((uint32_t)v[u & 1][k][h]);
+                            s1 = s1 + __uint_as_float((uint32_t)(v[u & 1][k][h] >> 32));
                         }
+                        acc[blk / FN][blk % FN][2 * (h0 + h)] = s0;
+                        acc[blk / FN][blk % FN][2 * (h0 + h) + 1] = s1;
+                    }
+                    __builtin_amdgcn_sched_barrier(0);  // no unit's loads move above an earlier unit's sums
+                }
+            };
+            if (ns == 2) {
+                reduce_pipelined(ic<2>{});
+            } else if (ns == 4) {
+                reduce_pipelined(ic<4>{});
+            } else {
 #pragma unroll
-                        for (int g = 0; g < G; ++g) {
-                            if (k0 + g >= ns) break;
+                for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-                            for (int h = 0; h < ACC / 2; ++h) {
-                                const float v0 = __uint_as_float((uint32_t)v[g][h]);
-                                const float v1 = __uint_as_float((uint32_t)(v[g][h] >> 32));
-                                sum[2 * h] = k0 + g == 0 ? v0 : sum[2 * h] + v0;
-                                sum[2 * h + 1] = k0 + g == 0 ? v1 : sum[2 * h + 1] + v1;
+                    for (int fn = 0; fn < FN; ++fn) {
+                        const size_t o = ((((size_t)wave * FM + fm) * FN + fn) * (ACC / 2)) * 128 + lane * 2;
+                        AccT sum;
+                        for (int k0 = 0; k0 < ns; k0 += G) {
+                            uint64_t v[G][ACC / 2];
+#pragma unroll
+                            for (int g = 0; g < G; ++g) {
+                                const int k = k0 + g < ns ? k0 + g : ns - 1;  // in range; unused past ns
+#pragma unroll
+                                for (int h = 0; h < ACC / 2; ++h)
+                                    v[g][h] = __hip_atomic_load(
+                                        reinterpret_cast<const uint64_t *>(ws0 + (size_t)k * (BM * BN) + o + h * 128),
+                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            }
+#pragma unroll
+                            for (int g = 0; g < G; ++g) {
+                                if (k0 + g >= ns) break;
+#pragma unroll
+                                for (int h = 0; h < ACC / 2; ++h) {
+                                    const float v0 = __uint_as_float((uint32_t)v[g][h]);
+                                    const float v1 = __uint_as_float((uint32_t)(v[g][h] >> 32));
+                                    sum[2 * h] = k0 + g == 0 ? v0 : sum[2 * h] + v0;
+                                    sum[2 * h + 1] = k0 + g == 0 ? v1 : sum[2 * h + 1] + v1;
+                                }
                             }
                         }
+                        acc[fm][fn] = sum;
                     }
-                    acc[fm][fn] = sum;
-                }
+            }
         }
 
         // Epilogue: activation on the fp32 accumulator, RNE to bf16, then the

@@ -7,7 +7,8 @@ check exactly the configuration that is timed."""
 #   C2: 128x64 64-66; 64x128 69; 64x64 75; 64x256 75; 256x64 80; 128x128 110
 #   C3: 256x256 395-428; 256x128 517; 128x256 521
 #   C4: 128x128 514-524; 256x128 525-545 (16x16x32 blocks, 8 waves: 554-560);
-#       256x256 539-547 (split 2)
+#       256x256 539-547 (split 2; 516-525 with the pipelined split-K sum,
+#       level with 128x128 then)
 #   C5: 128x128 303-313; 256x64 376; 64x256 381; 128x256 407; 256x128 416
 TILES = {
     "c1": (64, 64),
