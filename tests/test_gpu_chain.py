@@ -338,6 +338,29 @@ def test_split_k_256_tiles(rt):
         assert same_bits(out["pipelined"], out[m]), m
 
 
+@pytest.mark.parametrize("nsplit", [2, 4])
+@pytest.mark.parametrize("tile", BF16_TILES, ids=[f"{a}x{b}" for a, b in BF16_TILES])
+def test_split_k_two_and_four_partials(rt, tile, nsplit):
+    """Two or four partials per split tile take the software-pipelined sum,
+    whose unit size depends on the tile's wave sub-tile and MFMA block: on
+    every bf16 tile shape, a one-row-block chain whose first layer has two
+    tiles and 16 k steps per item (k = 16 k-step x nsplit) is split exactly
+    nsplit ways.  Pipelined and sequential runs give the same bits, the
+    result matches the oracle, and the arrival counters end at 0."""
+    bm, bn = tile
+    k_step = 128 if tile == (256, 256) else 64
+    K0 = 16 * k_step * nsplit
+    M, widths = bm, (K0, 2 * bn, bn)
+    X, Ws = gen.chain_inputs(M, widths, gen.BF16, 1.0, (1 / np.sqrt(K0), 1 / np.sqrt(2 * bn)), 97 + nsplit)
+    say("split-K sum", tile, "nsplit", nsplit, M, widths)
+    out, st = run_modes(rt, X, Ws, gen.BF16, tile, acts=[gen.ACT_GELU_TANH, gen.ACT_NONE], flags=all_flags(),
+                        modes=("pipelined", "sequential"), reps=2)
+    assert st["nsplit"][0] == nsplit and st["nsplit"][1] == 1, st["nsplit"]
+    ref = oracle.chain(X, Ws, gen.BF16, acts=[gen.ACT_GELU_TANH, gen.ACT_NONE])
+    assert oracle.rel_err(as_values(out["pipelined"], gen.BF16), ref) <= TOL[gen.BF16]
+    assert same_bits(out["pipelined"], out["sequential"])
+
+
 def test_split_k_many_partials(rt):
     """A long-k layer with two tiles is split into 16 items per tile, so the
     last item to arrive sums its partials in several groups of loads; the
