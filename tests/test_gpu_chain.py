@@ -111,7 +111,7 @@ def test_c1_fp32_parity_all_modes(rt):
     assert same_bits(out["pipelined"], out["microbatch"])
     assert same_bits(out["pipelined"], out["spatial"])
     # 16 tiles per layer leave most compute units idle, so the plan splits
-    # both fp32 layers along k (items of 64 k, k-range dependencies)
+    # both fp32 layers along k (items of at least 128 k, k-range dependencies)
     assert st["nsplit"][0] > 1 and st["nsplit"][1] > 1, st["nsplit"]
     assert st["nonzero_arrivals"] == 0
     # unsplit, the plan uses exactly the hand-derived C1 tile graph
@@ -121,6 +121,24 @@ def test_c1_fp32_parity_all_modes(rt):
     assert st1["n_tiles"] == 32 and st1["n_edges"] == 128
     assert oracle.rel_err(as_values(out1["pipelined"], cfg.dtype), ref) <= TOL[gen.F32]
     assert same_bits(out1["pipelined"], out1["sequential"])
+
+
+def test_fp32_split_many_partials(rt):
+    """An fp32 layer with two tiles and k = 4096 is split into 32 items of
+    128 k each, so the last item to arrive sums its partials in several
+    groups of loads, in split order: every mode gives the same bits, the
+    result matches the oracle, and the arrival counters end at 0."""
+    M, widths = 128, (4096, 64, 64)
+    X, Ws = gen.chain_inputs(M, widths, gen.F32, 1.0, (1 / 64, 1 / 8), 93)
+    say("fp32 split-K chain with many partials", M, widths)
+    out, st = run_modes(rt, X, Ws, gen.F32, (64, 64), flags=all_flags(),
+                        modes=("pipelined", "sequential", "microbatch"), mb_rows=64, reps=2)
+    say("nsplit", st["nsplit"], "items", st["n_tiles"])
+    assert st["nsplit"][0] > 4, st["nsplit"]
+    ref = oracle.chain(X, Ws, gen.F32)
+    assert oracle.rel_err(as_values(out["pipelined"], gen.F32), ref) <= TOL[gen.F32]
+    for m in ("sequential", "microbatch"):
+        assert same_bits(out["pipelined"], out[m]), m
 
 
 # ----------------------------------------------------------------------------- bf16 small

@@ -12,8 +12,8 @@ Traffic: FETCH_SIZE and WRITE_SIZE (KiB per dispatch, from two separate
 --pmc runs) of the persistent worker kernel, each scaled by the factor that
 maps the same counter of a plain 1 GiB device copy (torch's copy kernel,
 reading 1 GiB and writing 1 GiB) onto its known size.  A summary records the
-SHA-256 of the kernel source it was taken on; a summary taken on another
-kernel source is ignored (traffic null).
+SHA-256 of the kernel and planner sources it was taken on; a summary taken
+on other sources is ignored (traffic null).
 """
 import argparse
 import csv
@@ -23,7 +23,10 @@ import statistics
 import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCES = [os.path.join(PKG, "csrc", "cp_kernels.hip"), os.path.join(PKG, "csrc", "cp_device.h")]
+# The kernels and the host planner: the planner picks the split-K factors,
+# which change the traffic a launch moves, so a summary taken before a change
+# to either no longer describes the current launch.
+KERNEL_SOURCES = [os.path.join(PKG, "csrc", n) for n in ("cp_kernels.hip", "cp_device.h", "cp_chain.cpp")]
 COPY_BYTES = 1 << 30
 WORKER = "worker_kernel"
 
