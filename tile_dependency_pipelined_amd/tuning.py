@@ -4,7 +4,8 @@ check exactly the configuration that is timed."""
 
 # (tile_m, tile_n) per workload key of inputs.CONFIGS, chosen by the
 # pipelined time of each candidate, interleaved on one MI355X (microseconds):
-#   C2: 128x64 64-66; 64x128 69; 64x64 75; 64x256 75; 256x64 80; 128x128 110
+#   C2: 128x64 59-63; 64x128 60-61; 128x128 72; 64x64 75; 64x256 75;
+#       256x64 81; 256x128 98; 128x256 99; 256x256 115
 #   C3: 256x256 395-428; 256x128 517; 128x256 521
 #   C4: 128x128 514-524; 256x128 525-545 (16x16x32 blocks, 8 waves: 554-560);
 #       256x256 539-547 (split 2; 516-525 with the pipelined split-K sum,
