@@ -153,11 +153,12 @@ typedef struct cp_chain_stats_t {
  * scoreboard, queue, intermediates C_1..C_{L-1} (M x N_l each) and sizes the
  * persistent grid from occupancy.  Needs a HIP device (CP_ERR_NO_DEVICE).
  * Every width must be at most 2^22.
- * Split-K: a bf16 layer with fewer tiles than the persistent grid holds is
- * split along k into power-of-two ranges (items) until it fills the grid,
- * keeping at least 16 k-slabs per item and, beyond layer 1, ranges made of
- * whole producer tiles; an item then waits only on the producer tiles of its
- * own k range.  Items store fp32 partials into a plan-owned workspace and
+ * Split-K: a layer with fewer tiles than the persistent grid holds is split
+ * along k into power-of-two ranges (items) until it fills the grid, keeping
+ * at least 16 k steps per bf16 item (64 k, or 128 k for 256x256 tiles) or 4
+ * slabs of 32 k per fp32 item and, beyond layer 1, ranges made of whole
+ * producer tiles; an item then waits only on the producer tiles of its own
+ * k range.  Items store fp32 partials into a plan-owned workspace and
  * the last item of a tile to finish sums them in split order, so results do
  * not depend on timing and all modes agree bit for bit.  CP_FLAG_NO_SPLIT
  * turns it off; cp_chain_stats reports the split of each layer.
