@@ -41,7 +41,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="c3")
     ap.add_argument("--tile", default=None, help="override tile, e.g. 256x128")
-    ap.add_argument("--reps", type=int, default=20, help="reps per mode for the baseline comparison")
+    ap.add_argument("--reps", type=int, default=50, help="reps per mode for the baseline comparison")
+    ap.add_argument("--settle-s", type=float, default=2.0,
+                    help="seconds of back-to-back pipelined steps before the counted warm-up, so "
+                         "that the timed steps run at the clock the part holds under sustained load "
+                         "(reported under 'settle', never counted as warm-up or timed steps)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-modes", action="store_true", help="skip the baseline-mode comparison")
     ap.add_argument("--profile", action="store_true",
@@ -91,6 +95,17 @@ def main():
     def step(mode="pipelined", mb=0, p=plan):
         p.run(dX, dW, dY, mode=mode, microbatch_rows=mb, stream=stream)
 
+    # settle: the clock ramps over the first ~10 ms of heavy load, so a
+    # fixed duration of back-to-back steps runs first, then the warm-up
+    settle_steps, s0 = 0, time.perf_counter()
+    while time.perf_counter() - s0 < args.settle_s:
+        for _ in range(20):
+            step()
+        settle_steps += 20
+        torch.cuda.synchronize()
+    settle = {"seconds": round(time.perf_counter() - s0, 3), "steps": settle_steps,
+              "what": "back-to-back pipelined steps before the warm-up; not timed, not counted"}
+    log(f"settle: {settle_steps} steps in {settle['seconds']} s")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -115,6 +130,25 @@ def main():
     ev_ms = ev0.elapsed_time(ev1) / args.steps
     log(f"timed: {args.steps} steps, {wall_ms * 1e3:.1f} us/step wall, {ev_ms * 1e3:.1f} us/step events")
     kernel_ms = ev_ms
+
+    # steady-state check, right after the timed region and outside it: the
+    # same K steps again with an event between consecutive steps (each event
+    # adds its own stream stall, a few us, to the step it closes)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
+    for k in range(args.steps):
+        step()
+        evs[k + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [evs[k].elapsed_time(evs[k + 1]) * 1e3 for k in range(args.steps)]
+    srt = sorted(per)
+    per_step = {"first_us": round(per[0], 1), "median_us": round(statistics.median(per), 1),
+                "last_us": round(per[-1], 1), "min_us": round(srt[0], 1), "max_us": round(srt[-1], 1),
+                "p10_us": round(srt[len(srt) // 10], 1), "p90_us": round(srt[(9 * len(srt)) // 10], 1),
+                "steps": args.steps,
+                "what": "the timed steps repeated right after the timed region with an event "
+                        "between consecutive steps; each includes one event's stream stall"}
+    log("per step", per_step)
 
     # one isolated launch at a time, bracketed by the library's own events
     # (CP_FLAG_TIMING) -- includes the events' own stream stalls
@@ -153,6 +187,8 @@ def main():
                    "widths": list(cfg.widths), "tile": list(tile), "mode": "pipelined",
                    "workers": plan.n_workers, "tiles": plan.n_tiles},
         "wall_ms_per_step": round(wall_ms, 4),
+        "settle": settle,
+        "per_step_check": per_step,
     }
 
     if args.profile:
@@ -272,12 +308,21 @@ def compare_modes(plan, step, stream, cfg, tile, reps, torch, tuning):
                 ts[r].append(one(r[0], r[1], cold))
         for name in ("pipelined", "sequential", "spatial"):
             out[f"{name}_{tag}"] = summary(ts[(name, 0)])
+        # paired differences: run r of pipelined against run r of the other
+        # mode, both from the same round of the interleaved order
+        def paired(other):
+            d = sorted(a - b for a, b in zip(ts[("pipelined", 0)], ts[other]))
+            return {"median_us": round(statistics.median(d), 1), "p10_us": round(d[len(d) // 10], 1),
+                    "p90_us": round(d[(9 * len(d)) // 10], 1),
+                    "pipelined_faster_in": f"{sum(x < 0 for x in d)} of {len(d)} rounds"}
+        out[f"pipelined_minus_sequential_{tag}"] = paired(("sequential", 0))
         mbs = [r for r in runs if r[0] == "microbatch"]
         if mbs:
             sw = {str(r[1]): summary(ts[r]) for r in mbs}
             best = min(mbs, key=lambda r: sw[str(r[1])]["median_us"])
             out[f"microbatch_best_{tag}"] = dict(sw[str(best[1])], chunk_rows=best[1])
             out[f"microbatch_sweep_{tag}"] = {k: v["median_us"] for k, v in sw.items()}
+            out[f"pipelined_minus_microbatch_best_{tag}"] = paired(best)
         log(tag, {k: v for k, v in out.items() if k.endswith(tag)})
     del scrub
     return out
@@ -412,12 +457,12 @@ def cpu_baseline(cfg, X, Ws, rows):
     import numpy as np
     import oracle
     if rows <= 0:
-        # about 10 s of CPU work: rate from a short calibration sample
+        # about 15 s of CPU work: rate from a short calibration sample
         probe = min(cfg.M, 16)
         t0 = time.perf_counter()
         oracle.chain(X, Ws, cfg.dtype, acts=list(cfg.acts), rows=np.arange(probe, dtype=np.int64))
         per_row_s = (time.perf_counter() - t0) / probe
-        rows = int(max(1, min(cfg.M, 10.0 / per_row_s)))
+        rows = int(max(1, min(cfg.M, 15.0 / per_row_s)))
     sel = np.arange(rows, dtype=np.int64)
     t0 = time.perf_counter()
     oracle.chain(X, Ws, cfg.dtype, acts=list(cfg.acts), rows=sel)
@@ -427,7 +472,21 @@ def cpu_baseline(cfg, X, Ws, rows):
     return {"value": round(flops / dt / 1e12, 5), "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle", "sample": f"first {rows} of {cfg.M} rows of X through the whole chain "
                                         f"({dt:.2f} s)",
+            "cpu_model": cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS"),
             "latency_us_whole_batch_extrapolated": round(dt * cfg.M / rows * 1e6, 0)}
+
+
+def cpu_model():
+    """The host CPU's model name as the kernel reports it (what lscpu prints)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 if __name__ == "__main__":

@@ -196,10 +196,18 @@ int cp_chain_run(cp_chain *plan, const void *X, const void *const *W, void *Y,
 
 /*
  * cp_chain_stats -- synchronise with the plan's last run and report status,
- * timing and the scoreboard/queue invariants (every
- * counter ends at 0, every tile dequeued exactly once).  Without
- * CP_FLAG_TIMING it synchronises the last run's stream, which must still
- * exist; cp_chain_trace likewise.
+ * timing and the scoreboard/queue invariants into the caller's `out`.
+ * The invariants restate the dependency structure (§III-A; Fig. 1): every
+ * producer epilogue decrements the scoreboard entry of each consumer once,
+ * so after a complete run every counter has gone from the consumer's
+ * in-degree to exactly 0; the producer whose decrement reaches 0 pushes
+ * the consumer's ID once, and every pushed ID is taken once from the
+ * workqueue, so the queue holds a permutation of all tile IDs and each tile
+ * is dequeued exactly once.  Without CP_FLAG_TIMING it synchronises the last
+ * run's stream, which must still exist; cp_chain_trace likewise.
+ * Returns CP_ERR_INVALID_ARG for a NULL plan or `out`, the device status
+ * (CP_ERR_TIMEOUT) when a worker's wait expired, CP_ERR_HIP on a failed copy.
+ * The invariant fields are filled after pipelined and spatial runs only.
  */
 int cp_chain_stats(cp_chain *plan, cp_chain_stats_t *out);
 
@@ -218,8 +226,24 @@ int cp_chain_stats(cp_chain *plan, cp_chain_stats_t *out);
 #define CP_TRACE_WORDS 6
 int cp_chain_trace(cp_chain *plan, uint64_t *out, int64_t capacity);
 
+/*
+ * cp_chain_intermediate -- copy the stored output C_layer of GEMM `layer`
+ * (1 <= layer < L; the tiles that layer layer+1 consumes, §III-B running
+ * example: the first GEMM's output read by the second) of the plan's last
+ * run into `dst`, host or device memory of at least M x N_layer elements of
+ * the plan's dtype (row-major, `capacity` in bytes).  Synchronises with the
+ * last run first; the contents are undefined before the first run.  For the
+ * element-wise error of each intermediate against a reference.
+ * CP_ERR_INVALID_ARG for a NULL plan or dst, a layer out of range or a
+ * capacity too small; CP_ERR_HIP if the copy fails.
+ */
+int cp_chain_intermediate(cp_chain *plan, int32_t layer, void *dst, int64_t capacity);
+
 /* cp_chain_destroy -- wait for the device (the plan's last stream may be
- * gone) and free the plan.  NULL is a no-op. */
+ * gone) and free the plan: the dependency structure it allocated (§III-A:
+ * dependency array, scoreboard, workqueues), the intermediates, split-K
+ * partials, streams, events and cached graphs.  Caller memory (X, W, Y,
+ * streams) is untouched.  NULL is a no-op; always returns CP_OK. */
 int cp_chain_destroy(cp_chain *plan);
 
 /*
@@ -247,9 +271,16 @@ int cp_chain_tile_graph_split(int64_t M, int32_t n_layers, const int64_t *widths
                               int32_t tile_n, const int32_t *nsplit, int32_t *n_tiles, int32_t *n_edges,
                               int32_t *layer_off, int32_t *indeg, int32_t *dep_off, int32_t *dep_ids);
 
-/* static description of a status code */
+/* Diagnostics of the library itself (the pages define no error reporting;
+ * the timeout they name is the bound on a consumer's queue wait, §III-A
+ * workqueue polling):
+ * cp_chain_error_string -- static, never-NULL description of a status code
+ *   ("unknown status" for codes outside CP_OK .. CP_ERR_INVARIANT); the
+ *   string is owned by the library;
+ * cp_chain_last_error -- thread-local detail of the most recent failure on
+ *   the calling thread ("" if the last call succeeded); valid until the
+ *   thread's next call into the library. */
 const char *cp_chain_error_string(int code);
-/* thread-local detail of the most recent failure on this thread ("" if none) */
 const char *cp_chain_last_error(void);
 
 #ifdef __cplusplus

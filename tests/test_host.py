@@ -281,7 +281,28 @@ def test_degenerate_shapes_rejected(case, code):
 def test_null_handles_rejected():
     """Calls on a NULL plan return CP_ERR_INVALID_ARG (destroy is a no-op)."""
     for call in (lambda: nat.cp_chain_run(None, 0, [0], 0, None, nat.CP_MODE_PIPELINED),
-                 lambda: nat.cp_chain_stats(None), lambda: nat.cp_chain_trace(None, 4)):
+                 lambda: nat.cp_chain_stats(None), lambda: nat.cp_chain_trace(None, 4),
+                 lambda: nat.cp_chain_intermediate(None, 1, 0, 0)):
         with pytest.raises(nat.CpError) as e:
             call()
         assert e.value.code == nat.CP_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("M, widths, nsplit", [
+    (64, [64, 1 << 22, 1 << 22], None),          # 2^16 tiles per layer, 2^32 edges
+    (1 << 14, [64, 1 << 20, 1 << 20], None),     # 2^28 tiles per layer, 2^40 edges
+    (1 << 16, [1 << 22, 1 << 16], [1 << 12]),    # 2^20 tiles x 2^12 items each = 2^32 items
+])
+def test_graph_size_overflow_rejected(M, widths, nsplit):
+    """Shapes inside the per-dimension limits whose tile graph would not fit
+    32-bit indices (edges or work items beyond 2^31) are refused with
+    CP_ERR_SHAPE before anything is built, by the host-only builder and by
+    the planner, instead of overflowing the edge offsets."""
+    with pytest.raises(nat.CpError) as e:
+        nat.cp_chain_tile_graph(M, widths, 64, 64, nsplit=nsplit)
+    assert e.value.code == nat.CP_ERR_SHAPE
+    assert "too large" in nat.cp_chain_last_error()
+    if nsplit is None:
+        with pytest.raises(nat.CpError) as e:
+            nat.cp_chain_plan(M, widths, nat.CP_BF16, 64, 64)
+        assert e.value.code == nat.CP_ERR_SHAPE

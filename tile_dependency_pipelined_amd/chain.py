@@ -59,6 +59,12 @@ class Chain:
     def trace(self):
         return nat.cp_chain_trace(self.handle, self.n_tiles)
 
+    def intermediate(self, layer):
+        """Intermediate C_layer (1 <= layer < L) of the last run as a new device tensor."""
+        out = torch.empty((self.M, self.widths[layer]), dtype=self.torch_dtype, device="cuda")
+        nat.cp_chain_intermediate(self.handle, layer, out.data_ptr(), out.numel() * out.element_size())
+        return out
+
     def close(self):
         if self.handle:
             nat.cp_chain_destroy(self.handle)

@@ -78,6 +78,28 @@ int check_shape(int64_t M, int32_t L, const int64_t *widths, int32_t tile_m, int
     return CP_OK;
 }
 
+// Sizes of the tile graph in 64-bit arithmetic, before anything is built:
+// items T = sum_l nrb nbn_l nsplit_l, edges E = sum_l nrb nbn_l nbn_{l+1}
+// (a producer tile has one edge per consumer tile of its row-block, split
+// or not).  The graph holds them in int32 arrays (dep_off has T + 1
+// entries and its last one is E), so both, and T + E, must stay below
+// 2^31.
+int check_graph_size(int64_t M, int32_t L, const int64_t *widths, int32_t tile_m, int32_t tile_n,
+                     const int32_t *nsplit) {
+    const int64_t nrb = M / tile_m, lim = (int64_t)0x7FFFFFF0;
+    int64_t T = 0, E = 0;
+    for (int l = 0; l < L; ++l) {
+        const int64_t nbn = widths[l + 1] / tile_n, ns = nsplit ? nsplit[l] : 1;
+        T += nrb * nbn * ns;  // each factor < 2^31, nbn * ns <= 2^22 * 2^22 when ns divides K0
+        if (l + 1 < L) E += nrb * nbn * (widths[l + 2] / tile_n);
+        if (T > lim || E > lim) break;
+    }
+    if (T > lim || E > lim || T + E > lim)
+        return fail(CP_ERR_SHAPE, "tile graph too large: %lld work items and %lld dependency edges "
+                    "(the table is indexed with 32-bit integers)", (long long)T, (long long)E);
+    return CP_OK;
+}
+
 // Dependency table (§III-A): tile (l+1, i, j) waits on all N_l / tile_n tiles
 // (l, i, k) of row-block i, because its A operand is that whole row-block.
 // With split-K, item s of tile (l+1, i, j) reads only columns
@@ -121,8 +143,8 @@ void build_graph(int64_t M, int32_t L, const int64_t *widths, int32_t tile_m, in
 
 // Split-K factor per layer: a layer with fewer tiles than the persistent grid
 // holds is split into power-of-two k ranges until it fills the grid, keeping
-// at least 16 slabs per item and (beyond layer 0) k ranges that are whole
-// producer tiles.  fp32 layers are never split.
+// at least 16 k steps per bf16 item (4 slabs of 32 k per fp32 item) and
+// (beyond layer 0) k ranges that are whole producer tiles.
 void choose_splits(int64_t M, int32_t L, const int64_t *widths, int32_t tile_m, int32_t tile_n, int32_t dtype,
                    int32_t k_step, int32_t capacity, bool allow, int32_t *ns) {
     const int64_t nrb = M / tile_m;
@@ -351,6 +373,8 @@ int cp_chain_tile_graph_split(int64_t M, int32_t n_layers, const int64_t *widths
                 return fail(CP_ERR_SHAPE, "nsplit[%d] = %d must be >= 1 and divide %lld", l, nsplit[l],
                             (long long)div);
         }
+    rc = check_graph_size(M, n_layers, widths, tile_m, tile_n, nsplit);
+    if (rc) return rc;
     TileGraph g;
     try {
         build_graph(M, n_layers, widths, tile_m, tile_n, nsplit, g);
@@ -378,6 +402,8 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
         return fail(CP_ERR_UNSUPPORTED, "no %s kernel for tile %dx%d", dtype == CP_BF16 ? "bf16" : "fp32",
                     tile_m, tile_n);
     int rc = check_shape(M, n_layers, widths, tile_m, tile_n, var->k_step);
+    if (rc) return rc;
+    rc = check_graph_size(M, n_layers, widths, tile_m, tile_n, nullptr);  // again once splits are chosen
     if (rc) return rc;
     if (acts)
         for (int l = 0; l < n_layers; ++l)
@@ -420,6 +446,7 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
     if (per_cu < 1) return bail(fail(CP_ERR_UNSUPPORTED, "kernel cannot be resident (occupancy 0)"));
     choose_splits(M, n_layers, widths, tile_m, tile_n, dtype, var->k_step, per_cu * cus,
                   !(flags & CP_FLAG_NO_SPLIT), p->nsplit);
+    if (int rc3 = check_graph_size(M, n_layers, widths, tile_m, tile_n, p->nsplit)) return bail(rc3);
     try {
         build_graph(M, n_layers, widths, tile_m, tile_n, p->nsplit, p->g);
     } catch (const std::bad_alloc &) {
@@ -676,7 +703,11 @@ int enqueue_spatial(cp_chain *p, const void *X, const void *const *W, void *Y, h
     // set, which never waits on it, so the in-order streams cannot deadlock
     for (int l = 0; l < p->L; ++l) {
         const cp::ChainArgs a = make_args(p, X, W, Y, p->cur, CP_MODE_SPATIAL, 1, l);
-        CP_HIP(p->var->launch_worker(a, p->sp_workers[l], false, p->sp_stream[l % 2]));
+        const hipError_t e = p->var->launch_worker(a, p->sp_workers[l], false, p->sp_stream[l % 2]);
+        if (e == hipErrorCooperativeLaunchTooLarge)
+            return fail(CP_ERR_UNSUPPORTED, "spatial grid of layer %d (%d workers) exceeds what the device holds "
+                        "at once", l, p->sp_workers[l]);
+        CP_HIP(e);
     }
     for (int k = 0; k < p->n_sets; ++k) {
         CP_HIP(hipEventRecord(p->sp_join[k], p->sp_stream[k]));
@@ -732,7 +763,11 @@ int cp_chain_run(cp_chain *p, const void *X, const void *const *W, void *Y, void
             CP_HIP(cp::launch_reset(make_args(p, nullptr, nullptr, nullptr, p->cur, mode, layout), s));
         if (timed && (p->flags & CP_FLAG_POISON)) CP_HIP(hipEventRecord(p->ev_kernel, s));
         if (mode == CP_MODE_PIPELINED) {
-            CP_HIP(p->var->launch_worker(a, p->n_workers, p->coop, s));
+            const hipError_t e = p->var->launch_worker(a, p->n_workers, p->coop, s);
+            if (e == hipErrorCooperativeLaunchTooLarge)
+                return fail(CP_ERR_UNSUPPORTED, "persistent grid of %d workers exceeds what the device holds at once "
+                            "for the launched kernel (every worker must be resident)", p->n_workers);
+            CP_HIP(e);
         } else {
             int rc = enqueue_spatial(p, X, W, Y, s);
             if (rc) return rc;
@@ -873,6 +908,21 @@ int cp_chain_trace(cp_chain *p, uint64_t *out, int64_t capacity) {
     int rc = wait_last(p);
     if (rc) return rc;
     CP_HIP(hipMemcpy(out, p->d_trace[p->last_copy], (size_t)p->g.T * 8 * cp::kTraceWords, hipMemcpyDeviceToHost));
+    return CP_OK;
+}
+
+int cp_chain_intermediate(cp_chain *p, int32_t layer, void *dst, int64_t capacity) {
+    g_last_error.clear();
+    if (!p || !dst) return fail(CP_ERR_INVALID_ARG, "plan or dst is NULL");
+    if (layer < 1 || layer >= p->L)
+        return fail(CP_ERR_INVALID_ARG, "layer %d: a %d-layer chain has intermediates C_1 .. C_%d", layer, p->L,
+                    p->L - 1);
+    const size_t bytes = p->inter_bytes[layer - 1];
+    if (capacity < 0 || (uint64_t)capacity < bytes)
+        return fail(CP_ERR_INVALID_ARG, "capacity %lld < %zu bytes of C_%d", (long long)capacity, bytes, layer);
+    int rc = wait_last(p);
+    if (rc) return rc;
+    CP_HIP(hipMemcpy(dst, p->inter[layer - 1], bytes, hipMemcpyDefault));
     return CP_OK;
 }
 

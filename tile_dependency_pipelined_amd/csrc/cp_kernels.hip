@@ -1137,8 +1137,28 @@ __global__ void poison_kernel(uint32_t *p, size_t words, uint32_t pattern) {
 // ----------------------------------------------------------------------------
 // Launchers and the variant table
 // ----------------------------------------------------------------------------
+// Workgroups of this instantiation the current device holds at once (its
+// occupancy times the compute units), computed once per process.
+template <class Body, bool SPLIT>
+int resident_capacity() {
+    static const int cap = [] {
+        int occ = 0, dev = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, worker_kernel<Body, SPLIT>, Body::NT, 0) !=
+                hipSuccess ||
+            hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        return occ * cus;
+    }();
+    return cap;
+}
+
+// The queue protocol's forward progress needs every worker resident, so a
+// grid larger than the launched instantiation's capacity is refused
+// (hipErrorCooperativeLaunchTooLarge) instead of launched.
 template <class Body, bool SPLIT>
 hipError_t launch_worker_s(const ChainArgs &a, int grid, bool cooperative, hipStream_t s) {
+    if (grid > resident_capacity<Body, SPLIT>()) return hipErrorCooperativeLaunchTooLarge;
     if (!cooperative) {
         hipLaunchKernelGGL((worker_kernel<Body, SPLIT>), dim3(grid), dim3(Body::NT), 0, s, a);
         return hipGetLastError();

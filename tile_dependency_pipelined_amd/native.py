@@ -36,7 +36,7 @@ CP_MAX_LAYERS = 8
 
 # every symbol include/cp_chain.h declares
 EXPORTS = ("cp_chain_plan", "cp_chain_run", "cp_chain_stats", "cp_chain_trace",
-           "cp_chain_destroy", "cp_chain_tile_graph", "cp_chain_tile_graph_split",
+           "cp_chain_intermediate", "cp_chain_destroy", "cp_chain_tile_graph", "cp_chain_tile_graph_split",
            "cp_chain_error_string", "cp_chain_last_error")
 
 
@@ -94,6 +94,8 @@ _lib.cp_chain_stats.restype = ctypes.c_int
 _lib.cp_chain_stats.argtypes = [_vp, ctypes.POINTER(cp_chain_stats_t)]
 _lib.cp_chain_trace.restype = ctypes.c_int
 _lib.cp_chain_trace.argtypes = [_vp, ctypes.POINTER(ctypes.c_uint64), _i64]
+_lib.cp_chain_intermediate.restype = ctypes.c_int
+_lib.cp_chain_intermediate.argtypes = [_vp, _i32, _vp, _i64]
 _lib.cp_chain_destroy.restype = ctypes.c_int
 _lib.cp_chain_destroy.argtypes = [_vp]
 _lib.cp_chain_tile_graph.restype = ctypes.c_int
@@ -167,6 +169,12 @@ def cp_chain_trace(plan, n_tiles):
     buf = (ctypes.c_uint64 * (CP_TRACE_WORDS * n_tiles))()
     _check(_lib.cp_chain_trace(plan, buf, CP_TRACE_WORDS * n_tiles), "cp_chain_trace")
     return list(buf)
+
+
+def cp_chain_intermediate(plan, layer, dst_ptr, capacity):
+    """Copy intermediate C_layer of the last run to host or device memory at dst_ptr."""
+    return _check(_lib.cp_chain_intermediate(plan, int(layer), int(dst_ptr), int(capacity)),
+                  "cp_chain_intermediate")
 
 
 def cp_chain_destroy(plan):
