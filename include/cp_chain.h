@@ -271,6 +271,36 @@ int cp_chain_tile_graph_split(int64_t M, int32_t n_layers, const int64_t *widths
                               int32_t tile_n, const int32_t *nsplit, int32_t *n_tiles, int32_t *n_edges,
                               int32_t *layer_off, int32_t *indeg, int32_t *dep_off, int32_t *dep_ids);
 
+/*
+ * cp_chain_run_noalloc -- for callers that cannot allocate (code that may run
+ * under stream capture, tight serving loops, harnesses that forbid
+ * hipMalloc): cp_chain_run in CP_MODE_PIPELINED with no plan and no
+ * allocation.  The arguments are those of cp_chain_plan (flags 0) followed by
+ * those of cp_chain_run; the split factors, persistent grid and kernels are
+ * the ones a plan of that shape uses, so Y is bit for bit what
+ * cp_chain_plan + cp_chain_run give.  Every piece of device state the run
+ * needs (dependency table, queues, scoreboard, intermediates, split-K
+ * partials) lives in one fixed device array of 64 MiB held by each device the
+ * library runs on until the process ends; the dependency table is written
+ * on the device by a setup kernel when the shape differs from the previous
+ * call's on that device.  No hipMalloc, hipFree or other allocation happens
+ * on any path.
+ *   status  NULL: the call only enqueues on `stream` and returns;
+ *           non-NULL: it also synchronises `stream` and stores the run's
+ *           device status there (CP_OK, or CP_ERR_TIMEOUT if a worker's wait
+ *           expired, which is also the return value).
+ * Errors: the plan's argument errors (CP_ERR_INVALID_ARG, CP_ERR_SHAPE,
+ * CP_ERR_UNSUPPORTED, CP_ERR_NO_DEVICE); CP_ERR_OOM when the chain needs more
+ * than the 64 MiB of state (e.g. intermediates beyond it), with the size in
+ * cp_chain_last_error; CP_ERR_HIP on a failed launch.  All calls on one
+ * device share its array, which keeps the last call's contents: calls whose
+ * runs may overlap on one device (other streams, other host threads'
+ * enqueues) race and must be ordered by the caller.
+ */
+int cp_chain_run_noalloc(int64_t M, int32_t n_layers, const int64_t *widths, int32_t dtype, int32_t tile_m,
+                         int32_t tile_n, const int32_t *acts, const void *X, const void *const *W, void *Y,
+                         void *stream, int32_t *status);
+
 /* Diagnostics of the library itself (the pages define no error reporting;
  * the timeout they name is the bound on a consumer's queue wait, §III-A
  * workqueue polling):

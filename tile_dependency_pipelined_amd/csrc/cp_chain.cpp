@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -23,17 +24,19 @@
 
 namespace {
 
-thread_local std::string g_last_error;
+// detail of the last failure on this thread: a fixed buffer, so that error
+// paths allocate nothing either
+thread_local char g_last_error[512];
 
 int fail(int code, const char *fmt, ...) {
-    char buf[512];
     va_list ap;
     va_start(ap, fmt);
-    vsnprintf(buf, sizeof buf, fmt, ap);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
     va_end(ap);
-    g_last_error = buf;
     return code;
 }
+
+void clear_error() { g_last_error[0] = 0; }
 
 #define CP_HIP(call)                                                                     \
     do {                                                                                 \
@@ -351,7 +354,7 @@ const char *cp_chain_error_string(int code) {
     }
 }
 
-const char *cp_chain_last_error(void) { return g_last_error.c_str(); }
+const char *cp_chain_last_error(void) { return g_last_error; }
 
 int cp_chain_tile_graph(int64_t M, int32_t n_layers, const int64_t *widths, int32_t tile_m,
                         int32_t tile_n, int32_t *n_tiles, int32_t *n_edges, int32_t *layer_off,
@@ -363,7 +366,7 @@ int cp_chain_tile_graph(int64_t M, int32_t n_layers, const int64_t *widths, int3
 int cp_chain_tile_graph_split(int64_t M, int32_t n_layers, const int64_t *widths, int32_t tile_m,
                               int32_t tile_n, const int32_t *nsplit, int32_t *n_tiles, int32_t *n_edges,
                               int32_t *layer_off, int32_t *indeg, int32_t *dep_off, int32_t *dep_ids) {
-    g_last_error.clear();
+    clear_error();
     int rc = check_shape(M, n_layers, widths, tile_m, tile_n, 0);
     if (rc) return rc;
     if (nsplit)
@@ -393,7 +396,7 @@ int cp_chain_tile_graph_split(int64_t M, int32_t n_layers, const int64_t *widths
 int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *widths,
                   int32_t dtype, int32_t tile_m, int32_t tile_n, const int32_t *acts,
                   uint32_t flags) {
-    g_last_error.clear();
+    clear_error();
     if (!out) return fail(CP_ERR_INVALID_ARG, "out is NULL");
     *out = nullptr;
     if (dtype != CP_F32 && dtype != CP_BF16) return fail(CP_ERR_INVALID_ARG, "dtype %d", dtype);
@@ -720,7 +723,7 @@ int enqueue_spatial(cp_chain *p, const void *X, const void *const *W, void *Y, h
 
 int cp_chain_run(cp_chain *p, const void *X, const void *const *W, void *Y, void *stream,
                  int32_t mode, int64_t microbatch_rows) {
-    g_last_error.clear();
+    clear_error();
     if (!p) return fail(CP_ERR_INVALID_ARG, "plan is NULL");
     if (!X || !W || !Y) return fail(CP_ERR_INVALID_ARG, "X, W or Y is NULL");
     for (int l = 0; l < p->L; ++l)
@@ -809,7 +812,7 @@ int wait_last(cp_chain *p) {
 }  // namespace
 
 int cp_chain_stats(cp_chain *p, cp_chain_stats_t *out) {
-    g_last_error.clear();
+    clear_error();
     if (!p || !out) return fail(CP_ERR_INVALID_ARG, "plan or out is NULL");
     memset(out, 0, sizeof *out);
     out->mode = p->last_mode;
@@ -900,7 +903,7 @@ int cp_chain_stats(cp_chain *p, cp_chain_stats_t *out) {
 }
 
 int cp_chain_trace(cp_chain *p, uint64_t *out, int64_t capacity) {
-    g_last_error.clear();
+    clear_error();
     if (!p || !out) return fail(CP_ERR_INVALID_ARG, "plan or out is NULL");
     if (!(p->flags & CP_FLAG_TRACE)) return fail(CP_ERR_INVALID_ARG, "plan was built without CP_FLAG_TRACE");
     if (capacity < cp::kTraceWords * (int64_t)p->g.T)
@@ -912,7 +915,7 @@ int cp_chain_trace(cp_chain *p, uint64_t *out, int64_t capacity) {
 }
 
 int cp_chain_intermediate(cp_chain *p, int32_t layer, void *dst, int64_t capacity) {
-    g_last_error.clear();
+    clear_error();
     if (!p || !dst) return fail(CP_ERR_INVALID_ARG, "plan or dst is NULL");
     if (layer < 1 || layer >= p->L)
         return fail(CP_ERR_INVALID_ARG, "layer %d: a %d-layer chain has intermediates C_1 .. C_%d", layer, p->L,
@@ -927,12 +930,263 @@ int cp_chain_intermediate(cp_chain *p, int32_t layer, void *dst, int64_t capacit
 }
 
 int cp_chain_destroy(cp_chain *p) {
-    g_last_error.clear();
+    clear_error();
     if (!p) return CP_OK;
     if (p->ran) (void)hipDeviceSynchronize();  // the last run's stream may be gone
     for (auto &s : p->side)
         if (s) (void)hipStreamSynchronize(s);
     release(p);
+    return CP_OK;
+}
+
+
+// ----------------------------------------------------------------------------
+// Allocation-free pipelined run: every piece of device state a pipelined run
+// needs (dependency table, queue image, two per-run state copies,
+// intermediates, split-K partials) lives in one file-scope device array, and
+// the dependency table is written on the device from its closed form, so a
+// call allocates neither device nor host memory.
+// ----------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;  // 64 MiB per device
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+constexpr int kStaticMaxDevices = 64;
+
+// Host-side bookkeeping per device: the scratch array's device address (the
+// array's name is only a host-side stand-in), the resident capacity of the
+// variant last used, and the shape whose tables the scratch holds, with the
+// state copy the next run of that shape uses.
+struct StaticDevice {
+    bool ready = false;
+    char *ptr = nullptr;
+    int cus = 0;
+    // tables in the scratch are valid for this shape
+    bool have_shape = false;
+    int64_t M = 0;
+    int32_t L = 0, dtype = 0, tile_m = 0, tile_n = 0;
+    int64_t widths[CP_MAX_LAYERS + 1] = {};
+    int cur = 0;
+};
+StaticDevice g_static[kStaticMaxDevices];
+std::mutex g_static_mu;
+
+// Layout of one chain's state inside the scratch array (byte offsets).
+struct StaticLayout {
+    cp::GraphDims g;
+    int nq = 1, n_workers = 0;
+    int32_t qbase[cp::kMaxQueues] = {}, qsize[cp::kMaxQueues] = {}, qfirst[cp::kMaxQueues] = {},
+            qworkers[cp::kMaxQueues] = {};
+    size_t o_ctl[2] = {}, o_score[2] = {}, o_queue[2] = {}, o_arrive[2] = {};
+    size_t o_indeg = 0, o_doff = 0, o_dids = 0, o_qinit = 0;
+    size_t o_inter[CP_MAX_LAYERS] = {}, o_ws[CP_MAX_LAYERS] = {};
+    size_t total = 0;
+};
+
+// Items of one row-block whose position p satisfies p mod nq == q.
+int32_t per_queue(int32_t per, int nq, int q) { return per > q ? (per - q + nq - 1) / nq : 0; }
+
+void static_layout(int64_t M, int32_t L, const int64_t *widths, int32_t dtype, int32_t tile_m, int32_t tile_n,
+                   const int32_t *nsplit, int n_workers, StaticLayout &s) {
+    cp::GraphDims &g = s.g;
+    memset(&g, 0, sizeof g);
+    g.L = L;
+    g.nrb = (int32_t)(M / tile_m);
+    for (int l = 0; l < L; ++l) {
+        g.nbn[l] = (int32_t)(widths[l + 1] / tile_n);
+        g.nsplit[l] = nsplit[l];
+        g.layer_off[l + 1] = g.layer_off[l] + g.nrb * g.nbn[l] * g.nsplit[l];
+        g.edge_off[l + 1] = g.edge_off[l] + (l + 1 < L ? g.nrb * g.nbn[l] * (int32_t)(widths[l + 2] / tile_n) : 0);
+    }
+    g.T = g.layer_off[L];
+    g.E = g.edge_off[L];
+    s.n_workers = n_workers;
+    s.nq = std::max(1, std::min({cp::kMaxQueues, 8, n_workers}));
+    int32_t base = 0;
+    for (int q = 0; q < s.nq; ++q) {
+        int32_t size = 0;
+        for (int l = 0; l < L; ++l) size += g.nrb * per_queue(g.nbn[l] * g.nsplit[l], s.nq, q);
+        s.qbase[q] = base;
+        s.qsize[q] = size;
+        s.qfirst[q] = g.nrb * per_queue(g.nbn[0] * g.nsplit[0], s.nq, q);
+        s.qworkers[q] = (n_workers - q + s.nq - 1) / s.nq;
+        base += size;
+    }
+    const size_t T = (size_t)g.T, E = (size_t)std::max(g.E, 1);
+    size_t off = 0;
+    for (int c = 0; c < 2; ++c) {
+        s.o_ctl[c] = off;    off = align_up(off + cp::kCtlWords * 4, 256);
+        s.o_score[c] = off;  off = align_up(off + T * 4, 256);
+        s.o_queue[c] = off;  off = align_up(off + T * 4, 256);
+        s.o_arrive[c] = off; off = align_up(off + T * 4, 256);
+    }
+    s.o_indeg = off; off = align_up(off + T * 4, 256);
+    s.o_doff = off;  off = align_up(off + (T + 1) * 4, 256);
+    s.o_dids = off;  off = align_up(off + E * 4, 256);
+    s.o_qinit = off; off = align_up(off + T * 4, 256);
+    const size_t es = dtype == CP_BF16 ? 2 : 4;
+    for (int l = 0; l + 1 < L; ++l) {
+        s.o_inter[l] = off;
+        off = align_up(off + (size_t)M * (size_t)widths[l + 1] * es, 256);
+    }
+    for (int l = 0; l < L; ++l)
+        if (nsplit[l] > 1) {
+            s.o_ws[l] = off;
+            off = align_up(off + (size_t)(g.layer_off[l + 1] - g.layer_off[l]) * tile_m * tile_n * 4, 256);
+        }
+    s.total = off;
+}
+
+}  // namespace
+
+int cp_chain_run_noalloc(int64_t M, int32_t n_layers, const int64_t *widths, int32_t dtype, int32_t tile_m,
+                         int32_t tile_n, const int32_t *acts, const void *X, const void *const *W, void *Y,
+                         void *stream, int32_t *status) {
+    clear_error();
+    if (status) *status = CP_OK;
+    if (dtype != CP_F32 && dtype != CP_BF16) return fail(CP_ERR_INVALID_ARG, "dtype %d", dtype);
+    const cp::Variant *var = cp::find_variant(dtype, tile_m, tile_n);
+    if (!var)
+        return fail(CP_ERR_UNSUPPORTED, "no %s kernel for tile %dx%d", dtype == CP_BF16 ? "bf16" : "fp32", tile_m,
+                    tile_n);
+    int rc = check_shape(M, n_layers, widths, tile_m, tile_n, var->k_step);
+    if (rc) return rc;
+    rc = check_graph_size(M, n_layers, widths, tile_m, tile_n, nullptr);
+    if (rc) return rc;
+    if (acts)
+        for (int l = 0; l < n_layers; ++l)
+            if (acts[l] != CP_ACT_NONE && acts[l] != CP_ACT_GELU_TANH)
+                return fail(CP_ERR_INVALID_ARG, "acts[%d] = %d", l, acts[l]);
+    if (!X || !W || !Y) return fail(CP_ERR_INVALID_ARG, "X, W or Y is NULL");
+    for (int l = 0; l < n_layers; ++l)
+        if (!W[l]) return fail(CP_ERR_INVALID_ARG, "W[%d] is NULL", l);
+    int dev = -1;
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) return fail(CP_ERR_NO_DEVICE, "no HIP device visible");
+    CP_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kStaticMaxDevices) return fail(CP_ERR_UNSUPPORTED, "device %d beyond %d", dev, kStaticMaxDevices);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    StaticDevice &sd = g_static[dev];
+    if (!sd.ready) {
+        // once per device, with that device current: the array's device
+        // address; kernels and copies use this, never the array's name
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(CP_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        CP_HIP(hipDeviceGetAttribute(&sd.cus, hipDeviceAttributeMultiprocessorCount, dev));
+        sd.ptr = static_cast<char *>(ptr);
+        sd.ready = true;
+    }
+    int per_cu = 0;
+    CP_HIP(var->occupancy(&per_cu));
+    if (per_cu < 1) return fail(CP_ERR_UNSUPPORTED, "kernel cannot be resident (occupancy 0)");
+    // the split factors and grid of cp_chain_plan for this shape
+    int32_t nsplit[CP_MAX_LAYERS] = {};
+    choose_splits(M, n_layers, widths, tile_m, tile_n, dtype, var->k_step, per_cu * sd.cus, true, nsplit);
+    rc = check_graph_size(M, n_layers, widths, tile_m, tile_n, nsplit);
+    if (rc) return rc;
+    int64_t T = 0;
+    for (int l = 0; l < n_layers; ++l) T += (M / tile_m) * (widths[l + 1] / tile_n) * nsplit[l];
+    const int n_workers = (int)std::max<int64_t>(1, std::min<int64_t>((int64_t)per_cu * sd.cus, T));
+    StaticLayout ly;
+    static_layout(M, n_layers, widths, dtype, tile_m, tile_n, nsplit, n_workers, ly);
+    if (ly.total > kStaticScratchBytes)
+        return fail(CP_ERR_OOM, "this chain needs %zu bytes of device state; the allocation-free entry point "
+                    "holds %zu (use cp_chain_plan / cp_chain_run)", ly.total, kStaticScratchBytes);
+
+    bool same = sd.have_shape && sd.M == M && sd.L == n_layers && sd.dtype == dtype && sd.tile_m == tile_m &&
+                sd.tile_n == tile_n;
+    for (int l = 0; same && l <= n_layers; ++l) same = sd.widths[l] == widths[l];
+
+    char *base = sd.ptr;
+    cp::ChainArgs a;
+    memset(&a, 0, sizeof a);
+    for (int l = 0; l < n_layers; ++l) {
+        cp::LayerDesc &d = a.layer[l];
+        d.A = l == 0 ? X : static_cast<const void *>(base + ly.o_inter[l - 1]);
+        d.W = W[l];
+        d.C = l + 1 == n_layers ? Y : static_cast<void *>(base + ly.o_inter[l]);
+        d.K = (int32_t)widths[l];
+        d.N = (int32_t)widths[l + 1];
+        d.nbn = ly.g.nbn[l];
+        d.act = acts ? acts[l] : CP_ACT_NONE;
+        d.coherent = l + 1 < n_layers ? 1 : 0;  // write-through release
+        d.tile_off = ly.g.layer_off[l];
+        d.ntiles = ly.g.layer_off[l + 1] - ly.g.layer_off[l];
+        d.nsplit = nsplit[l];
+        d.ws = nsplit[l] > 1 ? reinterpret_cast<float *>(base + ly.o_ws[l]) : nullptr;
+    }
+    a.L = n_layers;
+    a.T = ly.g.T;
+    a.flags = 0;
+    a.nq = ly.nq;
+    a.nworkers = n_workers;
+    a.fixed_queue = -1;
+    a.queue_by_layer = 0;
+    for (int q = 0; q < cp::kMaxQueues; ++q) {
+        a.qbase[q] = ly.qbase[q];
+        a.qsize[q] = ly.qsize[q];
+        a.qfirst[q] = ly.qfirst[q];
+        a.qworkers[q] = ly.qworkers[q];
+    }
+    a.first_formula = 1;
+    a.indeg = reinterpret_cast<const int32_t *>(base + ly.o_indeg);
+    a.dep_off = reinterpret_cast<const int32_t *>(base + ly.o_doff);
+    a.dep_ids = reinterpret_cast<const int32_t *>(base + ly.o_dids);
+    a.qinit = reinterpret_cast<const uint32_t *>(base + ly.o_qinit);
+    int clk_khz = 0;
+    if (hipDeviceGetAttribute(&clk_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || clk_khz <= 0)
+        clk_khz = 100000;
+    a.timeout_ticks = (uint64_t)clk_khz * 1000ull * 2ull;  // 2 s
+    auto point = [&](cp::ChainArgs &x, int c) {
+        const int n = c ^ 1;
+        x.ctl = reinterpret_cast<uint32_t *>(base + ly.o_ctl[c]);
+        x.score = reinterpret_cast<int32_t *>(base + ly.o_score[c]);
+        x.queue = reinterpret_cast<uint32_t *>(base + ly.o_queue[c]);
+        x.arrive = reinterpret_cast<uint32_t *>(base + ly.o_arrive[c]);
+        x.nxt_ctl = reinterpret_cast<uint32_t *>(base + ly.o_ctl[n]);
+        x.nxt_score = reinterpret_cast<int32_t *>(base + ly.o_score[n]);
+        x.nxt_queue = reinterpret_cast<uint32_t *>(base + ly.o_queue[n]);
+        x.nxt_arrive = reinterpret_cast<uint32_t *>(base + ly.o_arrive[n]);
+    };
+    if (!same) {
+        // a new shape: write its tables and reset both state copies
+        sd.have_shape = false;
+        point(a, 0);
+        CP_HIP(cp::launch_graph_setup(a, ly.g, s));
+        sd.cur = 0;
+    }
+    point(a, sd.cur);
+    const hipError_t e = var->launch_worker(a, n_workers, false, s);
+    if (e != hipSuccess) {
+        sd.have_shape = false;  // the copies' state is unknown: set up again next time
+        if (e == hipErrorCooperativeLaunchTooLarge)
+            return fail(CP_ERR_UNSUPPORTED, "persistent grid of %d workers exceeds what the device holds at once",
+                        n_workers);
+        return fail(CP_ERR_HIP, "worker launch: %s", hipGetErrorString(e));
+    }
+    const int used = sd.cur;
+    sd.cur ^= 1;  // this run's workers reset the other copy
+    sd.have_shape = true;
+    sd.M = M;
+    sd.L = n_layers;
+    sd.dtype = dtype;
+    sd.tile_m = tile_m;
+    sd.tile_n = tile_n;
+    for (int l = 0; l <= n_layers; ++l) sd.widths[l] = widths[l];
+    if (status) {
+        // synchronise and read the run's device status (CP_OK or CP_ERR_TIMEOUT)
+        uint32_t st = 0;
+        CP_HIP(hipMemcpyAsync(&st, base + ly.o_ctl[used] + (size_t)cp::kCtlStatus * 4, 4, hipMemcpyDeviceToHost, s));
+        CP_HIP(hipStreamSynchronize(s));
+        *status = (int32_t)st;
+        if (st != 0) return fail((int)(int32_t)st, "device status %d: %s", (int)(int32_t)st,
+                                 cp_chain_error_string((int)(int32_t)st));
+    }
     return CP_OK;
 }
 

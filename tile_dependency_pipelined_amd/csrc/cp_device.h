@@ -102,6 +102,20 @@ __host__ __device__ inline uint32_t first_item(int per, int nq, int q, uint32_t 
     return i * (uint32_t)per + (uint32_t)q + k * (uint32_t)nq;
 }
 
+// Closed-form description of a chain's tile graph and queue layout, from
+// which a device kernel writes the dependency table, the queue image and
+// both per-run state copies (the allocation-free entry point builds no host
+// tables).  The table is the one the host builder makes.
+struct GraphDims {
+    int32_t L;
+    int32_t nrb;                   // row-blocks
+    int32_t nbn[kMaxLayers];       // tiles per row-block of each layer
+    int32_t nsplit[kMaxLayers];    // items per tile of each layer
+    int32_t layer_off[kMaxLayers + 1];  // first item of each layer, then T
+    int32_t edge_off[kMaxLayers + 1];   // first edge of each layer's producers, then E
+    int32_t T, E;
+};
+
 // A compiled kernel variant (element type x tile shape).
 struct Variant {
     int dtype, tile_m, tile_n, k_step;
@@ -115,6 +129,9 @@ const Variant *find_variant(int dtype, int tile_m, int tile_n);
 const Variant *variant_list(int *count);
 
 hipError_t launch_reset(const ChainArgs &a, hipStream_t s);
+// Writes indeg, dep_off, dep_ids and qinit of `a` from `g`, and resets both
+// per-run state copies (a.queue/ctl/score/arrive and a.nxt_*).
+hipError_t launch_graph_setup(const ChainArgs &a, const GraphDims &g, hipStream_t s);
 hipError_t launch_poison(void *p, size_t bytes, int dtype, hipStream_t s);
 
 }  // namespace cp

@@ -1127,6 +1127,74 @@ __global__ void reset_kernel(ChainArgs a) {
     reset_copy(a, a.queue, a.ctl, a.score, a.deq_count, a.trace, a.arrive);
 }
 
+// The dependency table, queue image and both state copies, computed from
+// the closed form of the tile graph (the same table the host builder makes):
+//   indeg   item of layer l > 0: N_{l-1} / tile_n producer tiles over its
+//           layer's split, 0 in layer 0;
+//   dep_off producers are the first items of layers 0 .. L-2, each with one
+//           edge per consumer tile of its row-block, in item order;
+//   dep_ids edge e of producer tile (i, k) of layer l goes to consumer tile
+//           (i, j) of layer l+1, item k / (producer tiles per k range);
+//   qinit   queue q holds its first-layer items, cp::first_item order, then
+//           empty slots.
+// Grid-stride over items, edges and queue slots; no thread reads what
+// another writes.
+__global__ void graph_setup_kernel(ChainArgs a, GraphDims g) {
+    const int stride = gridDim.x * blockDim.x;
+    const int t0 = blockIdx.x * blockDim.x + threadIdx.x;
+    int32_t *indeg = const_cast<int32_t *>(a.indeg);
+    int32_t *dep_off = const_cast<int32_t *>(a.dep_off);
+    int32_t *dep_ids = const_cast<int32_t *>(a.dep_ids);
+    uint32_t *qinit = const_cast<uint32_t *>(a.qinit);
+    for (int t = t0; t < g.T; t += stride) {
+        int l = 0;
+        while (l + 1 < g.L && t >= g.layer_off[l + 1]) ++l;
+        const int loc = t - g.layer_off[l], ns = g.nsplit[l];
+        const int32_t d = l > 0 ? g.nbn[l - 1] / ns : 0;
+        indeg[t] = d;
+        a.score[t] = d;
+        a.nxt_score[t] = d;
+        a.arrive[t] = 0;
+        a.nxt_arrive[t] = 0;
+        dep_off[t] = g.edge_off[l] + (l + 1 < g.L ? ((loc + ns - 1) / ns) * g.nbn[l + 1] : 0);
+        // queue slot t
+        int q = 0;
+        while (q + 1 < a.nq && t >= a.qbase[q + 1]) ++q;
+        const int r = t - a.qbase[q];
+        const uint32_t v = r < a.qfirst[q]
+                               ? first_item(g.nbn[0] * g.nsplit[0], a.nq, q, (uint32_t)r)
+                               : kEmpty;
+        qinit[t] = v;
+        a.queue[t] = v;
+        a.nxt_queue[t] = v;
+    }
+    if (t0 == 0) dep_off[g.T] = g.E;
+    for (int e = t0; e < g.E; e += stride) {
+        int l = 0;
+        while (l + 2 < g.L && e >= g.edge_off[l + 1]) ++l;
+        const int le = e - g.edge_off[l];
+        const int nc = g.nbn[l + 1];
+        const int ptile = le / nc, j = le - ptile * nc;
+        const int i = ptile / g.nbn[l], k = ptile - i * g.nbn[l];
+        const int per_split = g.nbn[l] / g.nsplit[l + 1];
+        dep_ids[e] = g.layer_off[l + 1] + (i * nc + j) * g.nsplit[l + 1] + k / per_split;
+    }
+    if (t0 < kMaxQueues) {
+        const int q = t0;
+        // slots 0 .. (workers of queue q) - 1 are handed out statically
+        const uint32_t head = q < a.nq ? (uint32_t)a.qworkers[q] : 0u;
+        const uint32_t tail = q < a.nq ? (uint32_t)a.qfirst[q] : 0u;
+        a.ctl[ctl_head(q)] = head;
+        a.ctl[ctl_tail(q)] = tail;
+        a.nxt_ctl[ctl_head(q)] = head;
+        a.nxt_ctl[ctl_tail(q)] = tail;
+        if (q == 0) {
+            a.ctl[kCtlStatus] = 0;
+            a.nxt_ctl[kCtlStatus] = 0;
+        }
+    }
+}
+
 // Fill an intermediate with quiet NaN so that a premature read is visible.
 __global__ void poison_kernel(uint32_t *p, size_t words, uint32_t pattern) {
     const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -1353,6 +1421,15 @@ hipError_t launch_reset(const ChainArgs &a, hipStream_t s) {
     if (grid > 1024) grid = 1024;
     if (grid < 1) grid = 1;
     hipLaunchKernelGGL(reset_kernel, dim3(grid), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_graph_setup(const ChainArgs &a, const GraphDims &g, hipStream_t s) {
+    const int n = g.T > g.E ? g.T : g.E;
+    int grid = (n + kThreads - 1) / kThreads;
+    if (grid > 1024) grid = 1024;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL(graph_setup_kernel, dim3(grid), dim3(kThreads), 0, s, a, g);
     return hipGetLastError();
 }
 

@@ -36,7 +36,7 @@ CP_MAX_LAYERS = 8
 
 # every symbol include/cp_chain.h declares
 EXPORTS = ("cp_chain_plan", "cp_chain_run", "cp_chain_stats", "cp_chain_trace",
-           "cp_chain_intermediate", "cp_chain_destroy", "cp_chain_tile_graph", "cp_chain_tile_graph_split",
+           "cp_chain_intermediate", "cp_chain_destroy", "cp_chain_run_noalloc", "cp_chain_tile_graph", "cp_chain_tile_graph_split",
            "cp_chain_error_string", "cp_chain_last_error")
 
 
@@ -96,6 +96,9 @@ _lib.cp_chain_trace.restype = ctypes.c_int
 _lib.cp_chain_trace.argtypes = [_vp, ctypes.POINTER(ctypes.c_uint64), _i64]
 _lib.cp_chain_intermediate.restype = ctypes.c_int
 _lib.cp_chain_intermediate.argtypes = [_vp, _i32, _vp, _i64]
+_lib.cp_chain_run_noalloc.restype = ctypes.c_int
+_lib.cp_chain_run_noalloc.argtypes = [_i64, _i32, _pi64, _i32, _i32, _i32, _pi32, _vp, ctypes.POINTER(_vp), _vp,
+                                      _vp, _pi32]
 _lib.cp_chain_destroy.restype = ctypes.c_int
 _lib.cp_chain_destroy.argtypes = [_vp]
 _lib.cp_chain_tile_graph.restype = ctypes.c_int
@@ -175,6 +178,19 @@ def cp_chain_intermediate(plan, layer, dst_ptr, capacity):
     """Copy intermediate C_layer of the last run to host or device memory at dst_ptr."""
     return _check(_lib.cp_chain_intermediate(plan, int(layer), int(dst_ptr), int(capacity)),
                   "cp_chain_intermediate")
+
+
+def cp_chain_run_noalloc(M, widths, dtype, tile_m, tile_n, acts, X_ptr, W_ptrs, Y_ptr, stream_ptr, sync=True):
+    """Pipelined run without a plan or any allocation.  With sync the call
+    waits for the run and raises on its device status; returns the status."""
+    L = len(widths) - 1
+    acts_c = (ctypes.c_int32 * L)(*[int(a) for a in acts]) if acts is not None else None
+    w = (ctypes.c_void_p * len(W_ptrs))(*[int(p) for p in W_ptrs])
+    st = ctypes.c_int32(0)
+    _check(_lib.cp_chain_run_noalloc(int(M), L, _i64_array(widths), int(dtype), int(tile_m), int(tile_n), acts_c,
+                                     int(X_ptr), w, int(Y_ptr), stream_ptr or None,
+                                     ctypes.byref(st) if sync else None), "cp_chain_run_noalloc")
+    return st.value
 
 
 def cp_chain_destroy(plan):
