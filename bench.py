@@ -222,9 +222,15 @@ def main():
         # copies are laid out for one queue layout at a time, and a pipelined
         # run after a spatial run on the same plan would first re-lay one
         # out (an extra reset launch inside its timed span)
-        with ch.Chain(cfg.M, cfg.widths, cfg.dtype, tile[0], tile[1], acts=list(cfg.acts)) as sp:
+        # the Lamport-sentinel release is a plan of its own too
+        with ch.Chain(cfg.M, cfg.widths, cfg.dtype, tile[0], tile[1], acts=list(cfg.acts)) as sp, \
+                ch.Chain(cfg.M, cfg.widths, cfg.dtype, tile[0], tile[1], acts=list(cfg.acts),
+                         flags=nat.CP_FLAG_LAMPORT) as lp:
             def step_modes(mode="pipelined", mb=0):
-                step(mode, mb, p=sp if mode == "spatial" else plan)
+                if mode == "lamport":
+                    step("pipelined", 0, p=lp)
+                else:
+                    step(mode, mb, p=sp if mode == "spatial" else plan)
             result["modes"] = compare_modes(plan, step_modes, stream, cfg, tile, args.reps, torch, tuning)
 
     if not args.profile:
@@ -272,7 +278,7 @@ def compare_modes(plan, step, stream, cfg, tile, reps, torch, tuning):
     alike; a short GPU sleep before the start event keeps host submission
     time out of the span.  Median, min, p10, p90 per mode."""
     scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-    runs = [("pipelined", 0), ("sequential", 0), ("spatial", 0)]
+    runs = [("pipelined", 0), ("sequential", 0), ("spatial", 0), ("lamport", 0)]
     runs += [("microbatch", m) for m in tuning.chunk_sweep(cfg.M, tile[0])]
 
     def one(mode, mb, cold):
@@ -306,7 +312,7 @@ def compare_modes(plan, step, stream, cfg, tile, reps, torch, tuning):
             k = rep % len(runs)
             for r in runs[k:] + runs[:k]:
                 ts[r].append(one(r[0], r[1], cold))
-        for name in ("pipelined", "sequential", "spatial"):
+        for name in ("pipelined", "sequential", "spatial", "lamport"):
             out[f"{name}_{tag}"] = summary(ts[(name, 0)])
         # paired differences: run r of pipelined against run r of the other
         # mode, both from the same round of the interleaved order
@@ -316,6 +322,7 @@ def compare_modes(plan, step, stream, cfg, tile, reps, torch, tuning):
                     "p90_us": round(d[(9 * len(d)) // 10], 1),
                     "pipelined_faster_in": f"{sum(x < 0 for x in d)} of {len(d)} rounds"}
         out[f"pipelined_minus_sequential_{tag}"] = paired(("sequential", 0))
+        out[f"pipelined_minus_lamport_{tag}"] = paired(("lamport", 0))
         mbs = [r for r in runs if r[0] == "microbatch"]
         if mbs:
             sw = {str(r[1]): summary(ts[r]) for r in mbs}

@@ -105,6 +105,19 @@ typedef struct cp_chain cp_chain; /* opaque plan */
 #define CP_FLAG_TIMING 256u
 /* never split a layer's k range (see cp_chain_plan: split-K) */
 #define CP_FLAG_NO_SPLIT 512u
+/* pipelined mode: Lamport-sentinel release instead of the default one
+ * (CTA-Pipelining §V-A, the Lamport synchronization alternative).  The plan
+ * keeps two copies of the intermediates, pre-filled with the sentinel -0.0
+ * (each run's workers fill the copy the next run uses); producers store
+ * their tiles with -0.0 replaced by +0.0 and decrement the counters
+ * without waiting for their stores to complete; consumers check every A
+ * fragment they read for the sentinel and re-read it from memory until it
+ * holds none.  Y is bit for bit that of every other mode.  Not with
+ * CP_FLAG_FENCE_RELEASE (CP_ERR_INVALID_ARG); CP_MODE_SPATIAL runs of such a
+ * plan return CP_ERR_UNSUPPORTED.  With CP_FLAG_DELAY_INJECT a quarter of
+ * producers release their tile before storing it (stored ~20 us later), so
+ * that consumers do read sentinels. */
+#define CP_FLAG_LAMPORT 1024u
 
 #define CP_MAX_LAYERS 8
 
@@ -132,6 +145,10 @@ typedef struct cp_chain_stats_t {
     int32_t nonzero_arrivals;/* split-K tiles whose arrival count did not end at 0        */
     int32_t nsplit[CP_MAX_LAYERS]; /* split-K items per tile of each layer (1 = no split) */
     int32_t fenced;          /* release protocol of the plan: 1 fence, 0 write-through   */
+    int32_t lamport;         /* 1 if the plan uses the Lamport-sentinel release           */
+    int32_t lamport_rereads; /* Lamport plans with CP_FLAG_DEBUG, after a pipelined run:
+                                slabs (bf16) or slab rows (fp32) in which a consumer found
+                                the sentinel and re-read (-1 if not recorded)             */
 } cp_chain_stats_t;
 
 /*

@@ -194,6 +194,102 @@ def test_signed_permutation_chain_exact_with_poison(rt, dtype, release):
     assert np.array_equal(as_values(out["spatial"], dtype), ref)
 
 
+@pytest.mark.parametrize("dtype", [gen.F32, gen.BF16], ids=["f32", "bf16"])
+def test_lamport_release_before_store_exact(rt, dtype):
+    """Lamport-sentinel release with a quarter of producers releasing their
+    tile before storing it (stored ~20 us later): consumers do read the
+    sentinel and must re-read until the data lands.  The signed-permutation
+    chain is exact, so the result must equal the oracle bit for bit, in
+    three consecutive runs (alternating intermediate copies, each refilled
+    by the previous run's workers), and equal the sequential mode's."""
+    f = rt_flags()
+    nat = rt["nat"]
+    tile = (64, 64) if dtype == gen.F32 else (128, 128)
+    n = 512 if dtype == gen.F32 else 1024
+    M = 4 * tile[0]
+    X = gen.normal_matrix((M, n), 1.0, 160, dtype)
+    Ws = [gen.signed_permutation(n, 161 + l, dtype, scale_pow2=s) for l, s in enumerate((1, -2, 0))]
+    say("lamport perm chain", dtype, tile, M, n)
+    out, st = run_modes(rt, X, Ws, dtype, tile, flags=all_flags() | f["DELAY"] | nat.CP_FLAG_LAMPORT,
+                        modes=("pipelined", "sequential"), reps=3)
+    assert st["lamport"] == 1 and st["fenced"] == 0, st
+    say("  waves that re-read a sentinel fragment in the last run:", st["lamport_rereads"])
+    assert st["lamport_rereads"] > 0, st   # consumers did see the sentinel
+    ref = oracle.chain(X, Ws, dtype)
+    assert np.array_equal(as_values(out["pipelined"], dtype), ref)
+    assert np.array_equal(as_values(out["sequential"], dtype), ref)
+
+
+@pytest.mark.parametrize("case", [
+    ("bf16 256x256, gelu", gen.BF16, 512, (1024, 768, 512), (256, 256), (1, 0)),
+    ("bf16 128x128 split-K both layers", gen.BF16, 128, (4096, 2048, 512), (128, 128), (1, 0)),
+    ("bf16 64x128 four layers", gen.BF16, 256, (256, 512, 384, 640, 256), (64, 128), (0, 1, 0, 0)),
+    ("fp32 64x64 split", gen.F32, 128, (512, 512, 512), (64, 64), (0, 0)),
+], ids=lambda c: c[0])
+def test_lamport_parity(rt, case):
+    """Lamport mode against the oracle on several bodies, split-K layers and
+    GeLU, with delayed (release-before-store) producers: within the bar,
+    bit-identical to the sequential mode, invariants exact, in repeated
+    runs."""
+    f = rt_flags()
+    nat = rt["nat"]
+    name, dtype, M, widths, tile, acts = case
+    L = len(widths) - 1
+    X, Ws = gen.chain_inputs(M, widths, dtype, 1.0, tuple(1 / np.sqrt(w) for w in widths[:-1]), 170)
+    say("lamport parity", name)
+    out, st = run_modes(rt, X, Ws, dtype, tile, acts=list(acts),
+                        flags=all_flags() | f["DELAY"] | nat.CP_FLAG_LAMPORT,
+                        modes=("pipelined", "sequential", "microbatch"), mb_rows=tile[0], reps=2)
+    ref = oracle.chain(X, Ws, dtype, acts=list(acts))
+    err = oracle.rel_err(as_values(out["pipelined"], dtype), ref)
+    say("  rel err", err, "nsplit", st["nsplit"][:L])
+    assert err <= TOL[dtype]
+    assert same_bits(out["pipelined"], out["sequential"])
+    assert same_bits(out["pipelined"], out["microbatch"])
+
+
+@pytest.mark.parametrize("dtype", [gen.F32, gen.BF16], ids=["f32", "bf16"])
+def test_lamport_input_negative_zero_is_data(rt, dtype):
+    """The caller's X may hold -0.0 (the sentinel's bit pattern): only
+    intermediates are checked, so a Lamport run with a third of X set to
+    -0.0 completes (no watchdog) with the sequential mode's bits."""
+    nat = rt["nat"]
+    M, widths = 256, (512, 512, 256)
+    X, Ws = gen.chain_inputs(M, widths, dtype, 1.0, (1 / np.sqrt(512), 1 / np.sqrt(512)), 172)
+    X = X.copy()
+    neg0 = np.uint16(0x8000) if dtype == gen.BF16 else np.float32(-0.0)
+    X.reshape(-1)[::3] = neg0
+    tile = (64, 64) if dtype == gen.F32 else (128, 128)
+    out, st = run_modes(rt, X, Ws, dtype, tile, flags=all_flags() | nat.CP_FLAG_LAMPORT,
+                        modes=("pipelined", "sequential"), reps=2)
+    assert st["status"] == 0 and st["lamport_rereads"] == 0, st
+    assert same_bits(out["pipelined"], out["sequential"])
+    assert oracle.rel_err(as_values(out["pipelined"], dtype), oracle.chain(X, Ws, dtype)) <= TOL[dtype]
+
+
+def test_lamport_plan_refuses_spatial_and_reads_back_its_copy(rt):
+    """A Lamport plan's spatial runs are refused; cp_chain_intermediate
+    returns the intermediate of the pipelined run's own copy, which equals
+    the sequential run's C_1 with -0.0 stored as +0.0."""
+    torch, ch, nat = rt["torch"], rt["chain"], rt["nat"]
+    M, widths = 256, (512, 1024, 256)
+    X, Ws = gen.chain_inputs(M, widths, gen.BF16, 1.0, (1 / np.sqrt(512), 1 / 32), 171)
+    dX, dW = ch.to_device(X, gen.BF16), [ch.to_device(w, gen.BF16) for w in Ws]
+    dY = torch.empty((M, widths[-1]), dtype=torch.bfloat16, device="cuda")
+    acts = [gen.ACT_GELU_TANH, gen.ACT_NONE]   # GeLU makes -0.0 for large negative inputs
+    with ch.Chain(M, widths, gen.BF16, 64, 128, acts=acts, flags=nat.CP_FLAG_LAMPORT) as c:
+        with pytest.raises(nat.CpError) as e:
+            c.run(dX, dW, dY, mode="spatial")
+        assert e.value.code == nat.CP_ERR_UNSUPPORTED
+        c.run(dX, dW, dY, mode="sequential")
+        seq = ch.to_host(c.intermediate(1), gen.BF16)
+        for _ in range(2):
+            c.run(dX, dW, dY, mode="pipelined")
+            lam = ch.to_host(c.intermediate(1), gen.BF16)
+            assert not np.any(lam == 0x8000)
+            assert np.array_equal(lam, np.where(seq == 0x8000, 0, seq))
+
+
 def test_gelu_chain_small(rt):
     M, widths = 128, (256, 512, 256)
     X, Ws = gen.chain_inputs(M, widths, gen.BF16, 1.0, (1 / 16, 1 / np.sqrt(512)), 70)

@@ -218,6 +218,14 @@ struct cp_chain {
     int last_copy = 0;                 // copy of the last pipelined run
     void *inter[CP_MAX_LAYERS] = {};
     size_t inter_bytes[CP_MAX_LAYERS] = {};
+    // CP_FLAG_LAMPORT: two sentinel-filled copies of the intermediates for the
+    // pipelined runs (copy c with per-run state copy c); `lam_clean[c]` says
+    // copy c holds only the sentinel (filled at plan time, or by the workers
+    // of the previous run); the baselines keep using `inter`
+    bool lamport = false;
+    void *lam[2][CP_MAX_LAYERS] = {};
+    bool lam_clean[2] = {false, false};
+    int inter_src = -1;                // intermediates of the last run: -1 `inter`, else lam copy
     hipStream_t side[2] = {nullptr, nullptr};
     hipStream_t cap = nullptr;         // origin stream of graph captures
     hipEvent_t ev_fork = nullptr, ev_join[2] = {nullptr, nullptr};
@@ -269,6 +277,9 @@ void release(cp_chain *p) {
     if (p->ev_stop) (void)hipEventDestroy(p->ev_stop);
     for (auto &b : p->inter)
         if (b) (void)hipFree(b);
+    for (auto &c : p->lam)
+        for (auto &b : c)
+            if (b) (void)hipFree(b);
     for (auto &b : p->ws)
         if (b) (void)hipFree(b);
     if (p->state) (void)hipFree(p->state);
@@ -292,6 +303,12 @@ cp::ChainArgs make_args(const cp_chain *p, const void *X, const void *const *W, 
         d.act = p->acts[l];
         d.coherent = ((mode == CP_MODE_PIPELINED || mode == CP_MODE_SPATIAL) && l + 1 < p->L &&
                       !p->fenced) ? 1 : 0;
+        if (p->lamport && mode == CP_MODE_PIPELINED) {
+            if (l > 0) d.A = p->lam[copy][l - 1];
+            if (l + 1 < p->L) d.C = p->lam[copy][l];
+            d.lam_in = l > 0 ? 1 : 0;
+            d.lam_out = l + 1 < p->L ? 1 : 0;
+        }
         d.tile_off = p->g.layer_off[l];
         d.ntiles = p->g.layer_off[l + 1] - p->g.layer_off[l];
         d.nsplit = p->g.nsplit[l];
@@ -332,6 +349,14 @@ cp::ChainArgs make_args(const cp_chain *p, const void *X, const void *const *W, 
     a.nxt_deq_count = (p->flags & CP_FLAG_DEBUG) ? p->d_deq[n] : nullptr;
     a.nxt_trace = (p->flags & CP_FLAG_TRACE) ? p->d_trace[n] : nullptr;
     a.timeout_ticks = p->timeout_ticks;
+    if (p->lamport && mode == CP_MODE_PIPELINED) {
+        // this run's workers fill the other copy for the next run
+        for (int l = 0; l + 1 < p->L; ++l) {
+            a.lam_fill[l] = p->lam[copy ^ 1][l];
+            a.lam_fill_bytes[l] = p->inter_bytes[l];
+        }
+        a.lam_pattern = cp::lamport_pattern(p->dtype);
+    }
     return a;
 }
 
@@ -414,11 +439,12 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
                 return fail(CP_ERR_INVALID_ARG, "acts[%d] = %d", l, acts[l]);
     const uint32_t known = CP_FLAG_DEBUG | CP_FLAG_TRACE | CP_FLAG_POISON | CP_FLAG_DELAY_INJECT | CP_FLAG_STARVE_LAST |
                            CP_FLAG_EAGER | CP_FLAG_COOPERATIVE | CP_FLAG_FENCE_RELEASE | CP_FLAG_TIMING |
-
-                           CP_FLAG_NO_SPLIT;
+                           CP_FLAG_NO_SPLIT | CP_FLAG_LAMPORT;
     if (flags & ~known) return fail(CP_ERR_INVALID_ARG, "unknown flags 0x%x", flags & ~known);
     if ((flags & CP_FLAG_STARVE_LAST) && n_layers < 2)
         return fail(CP_ERR_INVALID_ARG, "CP_FLAG_STARVE_LAST needs at least two layers");
+    if ((flags & CP_FLAG_LAMPORT) && (flags & CP_FLAG_FENCE_RELEASE))
+        return fail(CP_ERR_INVALID_ARG, "CP_FLAG_LAMPORT and CP_FLAG_FENCE_RELEASE are two different release protocols");
 
     int ndev = 0;
     const hipError_t de = hipGetDeviceCount(&ndev);
@@ -443,7 +469,7 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
     };
     if (hipGetDevice(&p->device) != hipSuccess) return bail(fail(CP_ERR_NO_DEVICE, "hipGetDevice failed"));
     int per_cu = 0, cus = 0;
-    if (var->occupancy(&per_cu) != hipSuccess ||
+    if (var->occupancy(&per_cu, (flags & CP_FLAG_LAMPORT) != 0) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device) != hipSuccess)
         return bail(fail(CP_ERR_HIP, "occupancy / CU count query failed"));
     if (per_cu < 1) return bail(fail(CP_ERR_UNSUPPORTED, "kernel cannot be resident (occupancy 0)"));
@@ -500,6 +526,16 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
         for (int l = 0; l + 1 < n_layers; ++l) {
             p->inter_bytes[l] = (size_t)M * (size_t)widths[l + 1] * es;
             CP_HIP(hipMalloc(&p->inter[l], p->inter_bytes[l]));
+        }
+        p->lamport = (flags & CP_FLAG_LAMPORT) != 0;
+        if (p->lamport) {
+            for (int c = 0; c < 2; ++c)
+                for (int l = 0; l + 1 < n_layers; ++l) {
+                    CP_HIP(hipMalloc(&p->lam[c][l], p->inter_bytes[l]));
+                    CP_HIP(cp::launch_fill(p->lam[c][l], p->inter_bytes[l], cp::lamport_pattern(dtype), nullptr));
+                }
+            CP_HIP(hipDeviceSynchronize());
+            p->lam_clean[0] = p->lam_clean[1] = true;
         }
         for (int l = 0; l < n_layers; ++l)  // split-K partials: one fp32 tile per item
             if (p->nsplit[l] > 1)
@@ -758,6 +794,8 @@ int cp_chain_run(cp_chain *p, const void *X, const void *const *W, void *Y, void
     if (timed) CP_HIP(hipEventRecord(p->ev_start, s));
     if (p->flags & CP_FLAG_POISON)
         for (int l = 0; l + 1 < p->L; ++l) CP_HIP(cp::launch_poison(p->inter[l], p->inter_bytes[l], p->dtype, s));
+    if (mode == CP_MODE_SPATIAL && p->lamport)
+        return fail(CP_ERR_UNSUPPORTED, "spatial mode has no Lamport-sentinel release (plan built with CP_FLAG_LAMPORT)");
     if (mode == CP_MODE_PIPELINED || mode == CP_MODE_SPATIAL) {
         // The state copy must have been reset for this mode's queue layout
         // (the previous run's workers reset it for their own layout).
@@ -765,12 +803,19 @@ int cp_chain_run(cp_chain *p, const void *X, const void *const *W, void *Y, void
         if (p->copy_layout[p->cur] != layout)
             CP_HIP(cp::launch_reset(make_args(p, nullptr, nullptr, nullptr, p->cur, mode, layout), s));
         if (timed && (p->flags & CP_FLAG_POISON)) CP_HIP(hipEventRecord(p->ev_kernel, s));
+        if (mode == CP_MODE_PIPELINED && p->lamport && !p->lam_clean[p->cur]) {
+            // this copy was not refilled by a previous run's workers
+            for (int l = 0; l + 1 < p->L; ++l)
+                CP_HIP(cp::launch_fill(p->lam[p->cur][l], p->inter_bytes[l], cp::lamport_pattern(p->dtype), s));
+        }
         if (mode == CP_MODE_PIPELINED) {
+            if (p->lamport) p->lam_clean[0] = p->lam_clean[1] = false;  // until the launch is in
             const hipError_t e = p->var->launch_worker(a, p->n_workers, p->coop, s);
             if (e == hipErrorCooperativeLaunchTooLarge)
                 return fail(CP_ERR_UNSUPPORTED, "persistent grid of %d workers exceeds what the device holds at once "
                             "for the launched kernel (every worker must be resident)", p->n_workers);
             CP_HIP(e);
+            if (p->lamport) p->lam_clean[p->cur ^ 1] = true;  // this run's workers fill it
         } else {
             int rc = enqueue_spatial(p, X, W, Y, s);
             if (rc) return rc;
@@ -779,8 +824,10 @@ int cp_chain_run(cp_chain *p, const void *X, const void *const *W, void *Y, void
         p->copy_layout[p->cur ^ 1] = layout;  // reset by this run's workers
         p->last_layout = layout;
         p->last_copy = p->cur;
+        p->inter_src = (p->lamport && mode == CP_MODE_PIPELINED) ? p->cur : -1;
         p->cur ^= 1;
     } else {
+        p->inter_src = -1;
         if (p->flags & CP_FLAG_EAGER) {
             int rc = enqueue_layers(p, a, mode, microbatch_rows, s);
             if (rc) return rc;
@@ -826,6 +873,8 @@ int cp_chain_stats(cp_chain *p, cp_chain_stats_t *out) {
     out->bad_dequeues = -1;
     out->order_violations = -1;
     out->fenced = p->fenced ? 1 : 0;
+    out->lamport = p->lamport ? 1 : 0;
+    out->lamport_rereads = -1;
     for (int l = 0; l < CP_MAX_LAYERS; ++l) out->nsplit[l] = l < p->L ? p->g.nsplit[l] : 0;
     out->last_run_ms = -1.0;
     out->last_kernel_ms = -1.0;
@@ -853,6 +902,7 @@ int cp_chain_stats(cp_chain *p, cp_chain_stats_t *out) {
     CP_HIP(hipMemcpy(score.data(), p->d_score[c], T * 4, hipMemcpyDeviceToHost));
     CP_HIP(hipMemcpy(queue.data(), p->d_queue[c], T * 4, hipMemcpyDeviceToHost));
     out->status = (int32_t)ctl[cp::kCtlStatus];
+    out->lamport_rereads = (p->lamport && (p->flags & CP_FLAG_DEBUG)) ? (int32_t)ctl[cp::kCtlRereads] : -1;
     const cp_chain::Layout &ly = p->lay[p->last_layout];
     out->n_queues = ly.nq;
     out->queues_drained = 1;
@@ -925,7 +975,8 @@ int cp_chain_intermediate(cp_chain *p, int32_t layer, void *dst, int64_t capacit
         return fail(CP_ERR_INVALID_ARG, "capacity %lld < %zu bytes of C_%d", (long long)capacity, bytes, layer);
     int rc = wait_last(p);
     if (rc) return rc;
-    CP_HIP(hipMemcpy(dst, p->inter[layer - 1], bytes, hipMemcpyDefault));
+    const void *src = p->inter_src >= 0 ? p->lam[p->inter_src][layer - 1] : p->inter[layer - 1];
+    CP_HIP(hipMemcpy(dst, src, bytes, hipMemcpyDefault));
     return CP_OK;
 }
 
@@ -1082,7 +1133,7 @@ int cp_chain_run_noalloc(int64_t M, int32_t n_layers, const int64_t *widths, int
         sd.ready = true;
     }
     int per_cu = 0;
-    CP_HIP(var->occupancy(&per_cu));
+    CP_HIP(var->occupancy(&per_cu, false));
     if (per_cu < 1) return fail(CP_ERR_UNSUPPORTED, "kernel cannot be resident (occupancy 0)");
     // the split factors and grid of cp_chain_plan for this shape
     int32_t nsplit[CP_MAX_LAYERS] = {};

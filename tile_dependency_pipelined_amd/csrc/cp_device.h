@@ -28,6 +28,7 @@ constexpr int kCtlLine = 32;                               // words per line
 __host__ __device__ constexpr int ctl_head(int q) { return (2 * q) * kCtlLine; }
 __host__ __device__ constexpr int ctl_tail(int q) { return (2 * q + 1) * kCtlLine; }
 constexpr int kCtlStatus = 2 * kMaxQueues * kCtlLine;      // 0 = ok, else a CP_ERR_* code
+constexpr int kCtlRereads = kCtlStatus + 1;                // Lamport debug: sentinel re-reads
 constexpr int kCtlWords = kCtlStatus + kCtlLine;
 
 constexpr int32_t kStatusTimeout = -6;  // == CP_ERR_TIMEOUT
@@ -46,6 +47,12 @@ struct LayerDesc {
     int32_t nsplit;    // split-K: items per output tile (1 = no split); item s of a
                        // tile covers k in [s K / nsplit, (s + 1) K / nsplit)
     float *ws;         // nsplit > 1: fp32 partial tiles, one per item
+    // Lamport-sentinel release (CP_FLAG_LAMPORT, pipelined mode):
+    int32_t lam_out;   // C is an intermediate pre-filled with the sentinel -0.0: stored
+                       // values have -0.0 replaced by +0.0, and the release does not wait
+                       // for the stores to complete
+    int32_t lam_in;    // A is such an intermediate: every A fragment is checked for the
+                       // sentinel before use and re-read from memory until it holds none
 };
 
 // Everything one launch needs, passed by value as the kernel argument.
@@ -84,6 +91,11 @@ struct ChainArgs {
     uint32_t *nxt_arrive;
     uint64_t *nxt_trace;
     uint64_t timeout_ticks;  // watchdog on a queue wait, 100 MHz ticks
+    // Lamport plans: the other copy of the intermediates, which this run's
+    // workers fill with the sentinel for the next run (null: nothing to fill)
+    void *lam_fill[kMaxLayers];
+    uint64_t lam_fill_bytes[kMaxLayers];  // multiples of 16
+    uint32_t lam_pattern;                 // sentinel word: two bf16 -0.0, or fp32 -0.0
 };
 
 // Queue that owns work item `id` of layer `l`: (column panel x nsplit +
@@ -122,7 +134,9 @@ struct Variant {
     int lds_bytes;
     hipError_t (*launch_worker)(const ChainArgs &, int grid, bool cooperative, hipStream_t);
     hipError_t (*launch_layer)(const ChainArgs &, int layer, int rb0, int nrb, hipStream_t);
-    hipError_t (*occupancy)(int *blocks_per_cu);
+    // workgroups of the persistent worker per compute unit, smallest over the
+    // instantiations a plan may launch (with or without split-K; Lamport or not)
+    hipError_t (*occupancy)(int *blocks_per_cu, bool lamport);
 };
 
 const Variant *find_variant(int dtype, int tile_m, int tile_n);
@@ -133,5 +147,9 @@ hipError_t launch_reset(const ChainArgs &a, hipStream_t s);
 // per-run state copies (a.queue/ctl/score/arrive and a.nxt_*).
 hipError_t launch_graph_setup(const ChainArgs &a, const GraphDims &g, hipStream_t s);
 hipError_t launch_poison(void *p, size_t bytes, int dtype, hipStream_t s);
+// Fill with a 32-bit pattern (the Lamport sentinel), written through to memory.
+hipError_t launch_fill(void *p, size_t bytes, uint32_t pattern, hipStream_t s);
+// Sentinel word of the Lamport release for an element type: -0.0 in every element.
+constexpr uint32_t lamport_pattern(int dtype) { return dtype == CP_BF16 ? 0x80008000u : 0x80000000u; }
 
 }  // namespace cp

@@ -69,9 +69,55 @@ __device__ __forceinline__ void wait_vmcnt() {
 template <int U>
 using ic = std::integral_constant<int, U>;
 
+// Lamport-sentinel checks.  A bf16 word holds two elements; either one equal
+// to the sentinel -0.0 (0x8000) marks data not yet stored in this run.
+__device__ __forceinline__ uint32_t has_sentinel_bf16x2(uint32_t w) {
+    return ((w & 0xFFFFu) == 0x8000u) | ((w >> 16) == 0x8000u);
+}
+__device__ __forceinline__ uint32_t has_sentinel_f32(float f) { return __float_as_uint(f) == 0x80000000u; }
+
+// Where a Lamport consumer reports a sentinel wait that exceeded the watchdog.
+struct LamWatch {
+    uint32_t *status;   // the run's status word, or null (baseline launches)
+    uint64_t timeout;   // 100 MHz ticks
+    uint32_t *rereads;  // CP_FLAG_DEBUG: count of fragments that found the sentinel, or null
+};
+
+// Re-read loop of a Lamport consumer: `n` 8-byte words at `src` (device
+// memory another XCD stores into), re-read after an agent-scope acquire
+// (which invalidates this XCD's L2, so a line read while it still held the
+// sentinel is not served again) until `clean` holds for every lane, or the
+// watchdog expires (the run's status becomes CP_ERR_TIMEOUT).
+template <int N, class Clean>
+__device__ __forceinline__ void lamport_reread(const uint64_t *src, uint64_t (&v)[N], const LamWatch &w,
+                                            Clean &&clean) {
+    const uint64_t t0 = wall_clock64();
+    if (w.rereads && (threadIdx.x & 63) == 0)
+        __hip_atomic_fetch_add(w.rereads, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (;;) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#pragma unroll
+        for (int e = 0; e < N; ++e) v[e] = __hip_atomic_load(src + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!__ballot(!clean(v))) return;
+        if (wall_clock64() - t0 > w.timeout) {
+            if (w.status)
+                __hip_atomic_store(w.status, (uint32_t)kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
+        __builtin_amdgcn_s_sleep(2);
+    }
+}
+
 // Fourth word of a raw (stride 0) buffer resource on gfx9-family parts:
 // 32-bit data format, so untyped dword loads are in range.
 constexpr int kRsrcWord3 = 0x00020000;
+
+// Four LDS words of a Lamport consumer: flags of the last three slabs'
+// checks and of a re-load round (zeroed at worker start and after each tile).
+__device__ __forceinline__ uint32_t *lamport_flags() {
+    __shared__ uint32_t flags[4];
+    return flags;
+}
 
 // ----------------------------------------------------------------------------
 // bf16 tile body: C[BM x BN] tile (i, j) of A[M][K] . W[K][N], slabs of BK
@@ -172,6 +218,56 @@ struct Bf16Body {
         }
     }
 
+    // The rare path of a bf16 Lamport consumer (every thread of the workgroup):
+    // some wave found the sentinel in the A part of the slab at `src` (bytes
+    // from the tile's first A row, `bytes` in range).  Each wave re-loads the A
+    // chunks it loads into LDS `As`, after an agent-scope acquire (which drops
+    // lines this XCD read while they still held the sentinel), and checks them
+    // again, until no wave finds a sentinel; three barriers per round, so that
+    // the vote word (flags[3]) is cleared before any wave marks it and read by
+    // every wave before it is cleared.  The watchdog is a round count, the same
+    // in every wave, so that all leave together.  Out of line: none of its
+    // state is live in the k loop.
+    struct LaneOffsets {
+        uint32_t v[A_PW];
+    };
+    __device__ __noinline__ static void lamport_reload_slab(char *As, char *src, uint32_t bytes, LaneOffsets a_off,
+                                                            LamWatch lw) {
+        uint32_t *lflag = lamport_flags();
+        const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const uint64_t rounds = lw.timeout / 100 + 1;  // a round takes well over 1 us
+        if (lw.rereads && tid == 0) __hip_atomic_fetch_add(lw.rereads, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (uint64_t round = 0;; ++round) {
+            __syncthreads();  // every wave has read the flags
+            if (tid == 0) lflag[3] = 0u;
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(src, 0, (int)bytes, kRsrcWord3);
+#pragma unroll
+            for (int q = 0; q < A_PW; ++q)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t *)(As + (q * NW + wave) * 1024), 16, a_off.v[q],
+                                                         0, 0, 0);
+            wait_vmcnt<0>();
+            __syncthreads();  // lflag[3] cleared before any wave marks it
+            uint32_t bad = 0;
+#pragma unroll
+            for (int q = 0; q < A_PW; ++q) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(As + (q * NW + wave) * 1024 + lane * 16);
+                bad |= has_sentinel_bf16x2(v.x) | has_sentinel_bf16x2(v.y) | has_sentinel_bf16x2(v.z) |
+                       has_sentinel_bf16x2(v.w);
+            }
+            if (__ballot(bad) != 0 && lane == 0) lflag[3] = 1u;
+            __syncthreads();
+            if (__builtin_amdgcn_readfirstlane(lflag[3]) == 0) break;
+            if (round >= rounds) {
+                if (lw.status && tid == 0)
+                    __hip_atomic_store(lw.status, (uint32_t)kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        __syncthreads();
+    }
+
     // `before_epilogue` runs in every thread once the main loop is done (the
     // worker takes its next ticket there).  Split-K (d.nsplit > 1): this
     // item multiplies k in [split K / nsplit, (split + 1) K / nsplit) and
@@ -181,9 +277,17 @@ struct Bf16Body {
     // SPLIT = false compiles the split-K path out (plans without a split
     // layer use that instantiation: the extra live state would cost the
     // persistent worker its scalar registers).
-    template <bool SPLIT, class Hook>
+    //
+    // LAM (Lamport consumer, d.lam_in): every A fragment is checked for the
+    // sentinel before the MFMAs that use it; a wave that finds one re-reads
+    // that step's A fragments from memory (lamport_reread), leaving the LDS
+    // copy alone, so the product never sees a sentinel and the result is
+    // the same bits as in every other mode.  `before_store` runs in every
+    // thread right before the tile's global stores.
+    template <bool SPLIT, bool LAM, class Hook, class StoreHook>
     __device__ __forceinline__ static bool run(const LayerDesc &d, int i, int j, int split, uint32_t *arrive,
-                                               char *const *stg, Hook &&before_epilogue) {
+                                               char *const *stg, Hook &&before_epilogue, StoreHook &&before_store,
+                                               const LamWatch &lw) {
         const uint16_t *__restrict__ A = static_cast<const uint16_t *>(d.A);
         const uint16_t *__restrict__ W = static_cast<const uint16_t *>(d.W);
         uint16_t *__restrict__ C = static_cast<uint16_t *>(d.C);
@@ -388,18 +492,64 @@ struct Bf16Body {
         // one pipeline step on the slab in stage u: slabs slab+1 .. slab+S-1
         // are in flight into the other stages; after the barrier stage u is
         // refilled with slab+S
+        // Lamport consumer: each wave checks the A chunks it loaded itself as
+        // soon as its own loads of the slab have landed (before the slab's
+        // barrier), and marks flag (slab mod 3) in LDS if one holds the
+        // sentinel; after the barrier every wave reads the flag, so the
+        // whole workgroup agrees without a barrier of its own.  A marked
+        // slab's A part is re-loaded after an agent-scope acquire (which
+        // drops lines this XCD read while they still held the sentinel)
+        // until no wave finds one, before any fragment of it is read.  Flag
+        // (slab mod 3) is cleared by thread 0 after the next barrier, when
+        // every wave has read it and two barriers before it is set again.
+        uint32_t *lflag = lamport_flags();
+        // The 8-wave bodies hold 128 accumulators per lane and have no
+        // registers to spare: there the chunks are read one at a time (the
+        // scheduling barrier keeps the compiler from batching the reads);
+        // the others read them all at once, one LDS round trip.
+        auto scan_own = [&](const char *As) -> bool {
+            uint32_t bad = 0;
+#pragma unroll
+            for (int q = 0; q < A_PW; ++q) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(As + (q * NW + wave) * 1024 + lane * 16);
+                bad |= has_sentinel_bf16x2(v.x) | has_sentinel_bf16x2(v.y) | has_sentinel_bf16x2(v.z) |
+                       has_sentinel_bf16x2(v.w);
+                if constexpr (NW == 8) __builtin_amdgcn_sched_barrier(0);
+            }
+            return __ballot(bad) != 0;
+        };
+        auto mark = [&](const char *As, int v) {
+            if constexpr (LAM)
+                if (scan_own(As) && lane == 0) lflag[v % 3] = 1u;
+        };
+        auto settle = [&](char *As, int v, int k0) {  // after the barrier that follows mark(As, v)
+            if constexpr (LAM) {
+                if (__builtin_amdgcn_readfirstlane(lflag[v % 3]) != 0) {
+                    LaneOffsets o;
+#pragma unroll
+                    for (int q = 0; q < A_PW; ++q) o.v[q] = a_off[q];
+                    lamport_reload_slab(As, a_base + (size_t)k0 * 2, a_bytes - 2u * k0, o, lw);
+                }
+                if (tid == 0) lflag[(v + 2) % 3] = 0u;  // read by every wave before this barrier
+            }
+        };
         auto step = [&](auto U, int slab) {
             constexpr int u = decltype(U)::value;
             head(stg[u]);
             wait_vmcnt<(S - 2) * PER>();
+            const bool more = slab + 1 < nk;      // stage u+1 holds slab + 1
+            if (more) mark(stg[(u + 1) % S], slab + 1);
             __syncthreads();
+            if (more) settle(stg[(u + 1) % S], slab + 1, (slab + 1) * BK);
             const int pre = slab + S < nk ? slab + S : nk - 1;
             tail(stg[u], pre * BK, stg[(u + 1) % S]);
         };
 #pragma unroll
         for (int u = 0; u < S; ++u) issue(stg[u], (u < nk ? u : nk - 1) * BK);
         wait_vmcnt<(S - 1) * PER>();
+        mark(stg[0], 0);
         __syncthreads();
+        settle(stg[0], 0, 0);
         load(stg[0], 0, f[0]);
         int slab = 0;
         for (; slab + S <= nk; slab += S) {
@@ -417,6 +567,8 @@ struct Bf16Body {
         }
         wait_vmcnt<0>();  // the trailing prefetches must land before the LDS is reused
         __syncthreads();
+        if constexpr (LAM)
+            if (tid == 0) lflag[0] = lflag[1] = lflag[2] = lflag[3] = 0u;  // for the next tile
         before_epilogue();
         const LayerDesc *dp = &d;
 
@@ -568,6 +720,9 @@ struct Bf16Body {
             return p;
         };
         const int act = dp->act;
+        // Lamport intermediates never hold the sentinel: -0.0 is stored as
+        // +0.0 (no stored bf16 equals 0xFFFFFFFF, so other layers keep theirs)
+        const uint32_t canon = dp->lam_out ? 0x8000u : 0xFFFFFFFFu;
         // A lane holds, per block, output row m = lane mod MI and groups of
         // four consecutive columns: MI = 32, column 8 gq + 4 (lane / 32) of
         // the block for accumulators 4 gq .. 4 gq + 3; MI = 16, column
@@ -586,10 +741,14 @@ struct Bf16Body {
                 const AccT &v = acc[fm][fn];
 #pragma unroll
                 for (int gq = 0; gq < ACC / 4; ++gq) {
-                    const uint32_t b0 = f32_to_bf16_rne(act_apply(v[4 * gq + 0], act));
-                    const uint32_t b1 = f32_to_bf16_rne(act_apply(v[4 * gq + 1], act));
-                    const uint32_t b2 = f32_to_bf16_rne(act_apply(v[4 * gq + 2], act));
-                    const uint32_t b3 = f32_to_bf16_rne(act_apply(v[4 * gq + 3], act));
+                    uint32_t b0 = f32_to_bf16_rne(act_apply(v[4 * gq + 0], act));
+                    uint32_t b1 = f32_to_bf16_rne(act_apply(v[4 * gq + 1], act));
+                    uint32_t b2 = f32_to_bf16_rne(act_apply(v[4 * gq + 2], act));
+                    uint32_t b3 = f32_to_bf16_rne(act_apply(v[4 * gq + 3], act));
+                    b0 = b0 == canon ? 0u : b0;
+                    b1 = b1 == canon ? 0u : b1;
+                    b2 = b2 == canon ? 0u : b2;
+                    b3 = b3 == canon ? 0u : b3;
                     *reinterpret_cast<uint2 *>(rowp + (((c0 + gq) ^ key) << 4)) =
                         make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
                 }
@@ -598,6 +757,7 @@ struct Bf16Body {
         __syncthreads();
         // An intermediate consumed by other XCDs while the run goes on is
         // stored at agent scope, which writes through this XCD's L2.
+        before_store();
         constexpr int RPI = NT / UPR;              // rows per store instruction
         constexpr int NI = BM / RPI;               // store instructions per lane
         const int t = tid / UPR, u = tid % UPR;
@@ -637,9 +797,13 @@ struct F32Body {
     // an fp32 partial, and the last item of the tile to arrive sums all
     // partials in split order and runs the epilogue.  Returns whether this
     // call completed the tile.
-    template <bool SPLIT, class Hook>
+    // LAM: the A values of every slab are checked for the sentinel -0.0 when
+    // they move from registers to LDS and re-read from memory until they
+    // hold none (see Bf16Body); `before_store` as in Bf16Body.
+    template <bool SPLIT, bool LAM, class Hook, class StoreHook>
     __device__ __forceinline__ static bool run(const LayerDesc &d, int i, int j, int split, uint32_t *arrive,
-                                               char *const *stg, Hook &&before_epilogue) {
+                                               char *const *stg, Hook &&before_epilogue, StoreHook &&before_store,
+                                               const LamWatch &lw) {
         const int K = d.K, N = d.N;
         const int kspan = SPLIT ? __builtin_amdgcn_readfirstlane(K / d.nsplit) : K;
         const int kbeg = SPLIT ? __builtin_amdgcn_readfirstlane(split * kspan) : 0;
@@ -679,6 +843,28 @@ struct F32Body {
             sl.b0 = *reinterpret_cast<const float4 *>(W + (size_t)(k0 + k) * N + col0 + n4 * 4);
             sl.b1 = *reinterpret_cast<const float4 *>(W + (size_t)(k0 + 16 + k) * N + col0 + n4 * 4);
         };
+        // Lamport consumer: the slab at k0 (relative to kbeg) holds no
+        // sentinel in its A values once this returns
+        auto validate = [&](Slab &sl, int k0) {
+            const uint32_t bad = has_sentinel_f32(sl.a0.x) | has_sentinel_f32(sl.a0.y) | has_sentinel_f32(sl.a0.z) |
+                                 has_sentinel_f32(sl.a0.w) | has_sentinel_f32(sl.a1.x) | has_sentinel_f32(sl.a1.y) |
+                                 has_sentinel_f32(sl.a1.z) | has_sentinel_f32(sl.a1.w);
+            if (__builtin_expect(__ballot(bad) != 0, 0)) {
+                const int r = tid >> 3, c4 = tid & 7;
+                auto clean = [](const uint64_t(&x)[2]) {
+                    return !(has_sentinel_f32(__uint_as_float((uint32_t)x[0])) |
+                             has_sentinel_f32(__uint_as_float((uint32_t)(x[0] >> 32))) |
+                             has_sentinel_f32(__uint_as_float((uint32_t)x[1])) |
+                             has_sentinel_f32(__uint_as_float((uint32_t)(x[1] >> 32))));
+                };
+                uint64_t v[2];
+                lamport_reread(reinterpret_cast<const uint64_t *>(A + (size_t)(row0 + r) * K + k0 + c4 * 4), v, lw, clean);
+                sl.a0 = *reinterpret_cast<const float4 *>(v);
+                lamport_reread(reinterpret_cast<const uint64_t *>(A + (size_t)(row0 + 32 + r) * K + k0 + c4 * 4), v, lw,
+                               clean);
+                sl.a1 = *reinterpret_cast<const float4 *>(v);
+            }
+        };
         auto lstore = [&](char *st, const Slab &sl) {
             float *As = reinterpret_cast<float *>(st);
             float *Bs = As + BK * AP;
@@ -713,6 +899,7 @@ struct F32Body {
         gload((1 < nk ? 1 : nk - 1) * BK, r1);
         gload((2 < nk ? 2 : nk - 1) * BK, r2);
         gload((3 < nk ? 3 : nk - 1) * BK, r3);
+        if constexpr (LAM) validate(r0, 0);
         lstore(stg[0], r0);
         __syncthreads();
         // slab ks sits in LDS stage ks mod 2 and its ring slot u = ks mod D is
@@ -723,7 +910,10 @@ struct F32Body {
             char *cur = (ks & 1) ? stg[1] : stg[0], *nxt = (ks & 1) ? stg[0] : stg[1];  // no dynamic indexing
             gload((ks + D < nk ? ks + D : nk - 1) * BK, ring(ic<u>{}));
             compute(cur);
-            if (ks + 1 < nk) lstore(nxt, ring(ic<un>{}));
+            if (ks + 1 < nk) {
+                if constexpr (LAM) validate(ring(ic<un>{}), (ks + 1) * BK);
+                lstore(nxt, ring(ic<un>{}));
+            }
             __syncthreads();
         };
         int ks = 0;
@@ -796,11 +986,15 @@ struct F32Body {
         const int act = d.act;
         const int m = row0 + wm * 32 + (lane & 31);
         float *crow = C + (size_t)m * N + col0 + wn * 32;
+        // Lamport intermediates never hold the sentinel: -0.0 is stored as +0.0
+        const uint32_t canon = d.lam_out ? 0x80000000u : 0u;
+        auto cf = [&](float x) { return __float_as_uint(x) == canon && canon ? 0.0f : x; };
+        before_store();
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
             const int n = g * 8 + (lane >> 5) * 4;
-            const float4 v = make_float4(act_apply(acc[4 * g + 0], act), act_apply(acc[4 * g + 1], act),
-                                         act_apply(acc[4 * g + 2], act), act_apply(acc[4 * g + 3], act));
+            const float4 v = make_float4(cf(act_apply(acc[4 * g + 0], act)), cf(act_apply(acc[4 * g + 1], act)),
+                                         cf(act_apply(acc[4 * g + 2], act)), cf(act_apply(acc[4 * g + 3], act)));
             if (d.coherent) {  // agent scope: writes through this XCD's L2
                 const uint64_t lo = (uint64_t)__float_as_uint(v.x) | ((uint64_t)__float_as_uint(v.y) << 32);
                 const uint64_t hi = (uint64_t)__float_as_uint(v.z) | ((uint64_t)__float_as_uint(v.w) << 32);
@@ -957,9 +1151,11 @@ __device__ __forceinline__ uint32_t first_slot(const ChainArgs &a, int q, uint32
 // Wave 0 then decrements the counter of every consumer (all in layer l+1),
 // one edge per lane, and pushes the consumers whose counter reached zero into
 // their owner queues, one tail atomic per queue.
+//   Lamport (the tile's layer has lam_out): no wait at all; consumers check
+//     the data itself for the sentinel and re-read it until it has landed.
 __device__ __forceinline__ void publish(const ChainArgs &a, uint32_t id, int l) {
     const bool fenced = (a.flags & CP_FLAG_FENCE_RELEASE) != 0;
-    if (!fenced) wait_vmcnt<0>();
+    if (!fenced && !a.layer[l].lam_out) wait_vmcnt<0>();
     __syncthreads();
     const int tid = threadIdx.x;
     if (tid >= 64) return;
@@ -1046,13 +1242,32 @@ __device__ __forceinline__ void reset_copy(const ChainArgs &a, uint32_t *queue, 
         // slots 0 .. (workers of queue q) - 1 are handed out statically
         ctl[ctl_head(q)] = q < a.nq ? (uint32_t)a.qworkers[q] : 0u;
         ctl[ctl_tail(q)] = q < a.nq ? (uint32_t)a.qfirst[q] : 0u;
-        if (q == 0) ctl[kCtlStatus] = 0;
+        if (q == 0) {
+            ctl[kCtlStatus] = 0;
+            ctl[kCtlRereads] = 0;
+        }
     }
 }
 
 // Lane 0 of wave 1: the worker's scheduler (takes tickets, polls slots),
 // while wave 0 is the publisher.
 constexpr int kSchedLane = 64;
+
+// Lamport plans: this worker's share of the sentinel fill of the other copy
+// of the intermediates (used by the next run), 16-byte stores written
+// through to memory.
+__device__ __forceinline__ void lamport_fill_share(const ChainArgs &a, int nt) {
+    const uint64_t pat = (uint64_t)a.lam_pattern | ((uint64_t)a.lam_pattern << 32);
+    const size_t stride = (size_t)a.nworkers * nt;
+    for (int l = 0; l < kMaxLayers && a.lam_fill[l]; ++l) {
+        uint64_t *p = static_cast<uint64_t *>(a.lam_fill[l]);
+        const size_t n = a.lam_fill_bytes[l] / 16;
+        for (size_t c = (size_t)blockIdx.x * nt + threadIdx.x; c < n; c += stride) {
+            __hip_atomic_store(p + 2 * c, pat, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(p + 2 * c + 1, pat, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
 
 // Persistent worker: loop prologue -> tile body -> publish until its queue
 // (blockIdx.x mod nq, so that workgroups dispatched round-robin over the
@@ -1064,8 +1279,16 @@ constexpr int kSchedLane = 64;
 // it).  The tile ID is broadcast through the first word of stage 0; the
 // second barrier guarantees every thread has read it before the body's
 // loads reuse stage 0.
-template <class Body, bool SPLIT>
-__global__ void __launch_bounds__(Body::NT) worker_kernel(ChainArgs a) {
+//
+// LAM (Lamport plans): consumers check their A data for the sentinel; each
+// worker, once its first tile is done, fills its share of the other copy of
+// the intermediates with the sentinel for the next run; with
+// CP_FLAG_DELAY_INJECT a fixed quarter of producers release their tile
+// BEFORE storing it and store it ~20 us later, so that consumers do read
+// sentinels (a test of the re-read path that the other protocols could not
+// survive).
+template <class Body, bool SPLIT, bool LAM>
+__device__ __forceinline__ void worker_loop(ChainArgs &a) {
     char *stg[5];
     Stages<Body>::get(stg);
     volatile uint32_t *slot = reinterpret_cast<volatile uint32_t *>(stg[0]);
@@ -1075,6 +1298,9 @@ __global__ void __launch_bounds__(Body::NT) worker_kernel(ChainArgs a) {
     // (the reset set each head past the workers' count)
     uint32_t ticket = a.fixed_queue >= 0 ? blockIdx.x : blockIdx.x / (unsigned)a.nq;
     bool first = true;
+    bool filled = !LAM;
+    const LamWatch lw{a.ctl + kCtlStatus, a.timeout_ticks, a.deq_count ? a.ctl + kCtlRereads : nullptr};
+    if (LAM && threadIdx.x < 4) lamport_flags()[threadIdx.x] = 0u;  // before the loop's first barrier
     for (;;) {
         if (sched) *slot = first ? first_slot(a, q, ticket) : wait_slot(a, q, ticket);
         first = false;
@@ -1087,9 +1313,30 @@ __global__ void __launch_bounds__(Body::NT) worker_kernel(ChainArgs a) {
         int l, i, j, split;
         decode(a, id, l, i, j, split);
         const uint32_t first_item_id = id - (uint32_t)split;  // the tile's first item carries its edges
-        const bool done = Body::template run<SPLIT>(a.layer[l], i, j, split, a.arrive + first_item_id, stg, [&] {
+        bool released = false;
+        auto next_ticket = [&] {
             if (sched) ticket = take_ticket(a, q);
-        });
+        };
+        auto store_hook = [&] {
+            if constexpr (LAM) {
+                if ((a.flags & CP_FLAG_DELAY_INJECT) && l + 1 < a.L && ((first_item_id * 2654435761u) >> 30) == 0) {
+                    publish(a, first_item_id, l);  // release first ...
+                    released = true;
+                    const uint64_t s0 = wall_clock64();
+                    while (wall_clock64() - s0 < 2000) __builtin_amdgcn_s_sleep(8);  // ... store ~20 us later
+                }
+            }
+        };
+        // Only a layer whose A is a Lamport intermediate checks it for the
+        // sentinel (the first layer's A is the caller's X, whose -0.0 is
+        // data); the other layers run the plain body.
+        bool done;
+        if (LAM && a.layer[l].lam_in)
+            done = Body::template run<SPLIT, true>(a.layer[l], i, j, split, a.arrive + first_item_id, stg, next_ticket,
+                                                   store_hook, lw);
+        else
+            done = Body::template run<SPLIT, false>(a.layer[l], i, j, split, a.arrive + first_item_id, stg,
+                                                    next_ticket, store_hook, lw);
         if (a.trace && threadIdx.x == 0) {
             a.trace[kTraceWords * (size_t)id + 2] = wall_clock64();
             a.trace[kTraceWords * (size_t)id + 5] = clock64();
@@ -1097,14 +1344,47 @@ __global__ void __launch_bounds__(Body::NT) worker_kernel(ChainArgs a) {
         // after publish's opening barrier wave 0 releases the tile while the
         // scheduler lane (wave 1) already waits for the next one; a split-K
         // item that did not complete its tile has nothing to release
-        if (done && l + 1 < a.L) publish(a, first_item_id, l);
+        if (done && l + 1 < a.L && !released) publish(a, first_item_id, l);
         else __syncthreads();
+        if (LAM && !filled) {
+            filled = true;
+            lamport_fill_share(a, Body::NT);
+        }
     }
+    if (LAM && !filled) lamport_fill_share(a, Body::NT);  // a worker that got no tile
     // Reset the other copy of the per-run state for the next run: nothing of
     // this run reads it, and the kernel boundary publishes it.  Done on the
     // way out, where a worker has nothing left to wait for, rather than
     // ahead of its first tile.
     reset_copy(a, a.nxt_queue, a.nxt_ctl, a.nxt_score, a.nxt_deq_count, a.nxt_trace, a.nxt_arrive);
+}
+
+// Waves per SIMD the LDS of a body allows (at most 2): the register budget
+// the Lamport worker is held to, so that its checks and re-read path never
+// cost it the occupancy of the plain worker.
+template <class Body>
+constexpr int lds_waves_per_simd() {
+    const int wgs = (160 * 1024) / (Body::S * Body::STAGE);
+    const int w = wgs * (Body::NT / 64) / 4;
+    return w < 1 ? 1 : (w > 2 ? 2 : w);
+}
+
+template <class Body, bool SPLIT, bool LAM>
+__global__ void __launch_bounds__(Body::NT) worker_kernel(ChainArgs a) {
+    static_assert(!LAM, "Lamport workers are lamport_worker_kernel");
+    worker_loop<Body, SPLIT, false>(a);
+}
+
+template <class Body, bool SPLIT>
+__global__ void __launch_bounds__(Body::NT, lds_waves_per_simd<Body>()) lamport_worker_kernel(ChainArgs a) {
+    worker_loop<Body, SPLIT, true>(a);
+}
+
+// The kernel of a (SPLIT, LAM) instantiation.
+template <class Body, bool SPLIT, bool LAM>
+constexpr auto worker_fn() {
+    if constexpr (LAM) return lamport_worker_kernel<Body, SPLIT>;
+    else return worker_kernel<Body, SPLIT, false>;
 }
 
 // One layer, one tile per workgroup, row-blocks [rb0, rb0 + nrb): the plain
@@ -1118,8 +1398,8 @@ __global__ void __launch_bounds__(Body::NT) layer_kernel(ChainArgs a, int l, int
     const int t = blockIdx.x;
     const int i = __builtin_amdgcn_readfirstlane(rb0 + t / per_rb), rem = t % per_rb;
     const int j = __builtin_amdgcn_readfirstlane(rem / d.nsplit), split = __builtin_amdgcn_readfirstlane(rem % d.nsplit);
-    (void)Body::template run<SPLIT>(d, i, j, split, a.arrive + d.tile_off + (i * d.nbn + j) * d.nsplit, stg,
-                                    [] {});
+    (void)Body::template run<SPLIT, false>(d, i, j, split, a.arrive + d.tile_off + (i * d.nbn + j) * d.nsplit,
+                                           stg, [] {}, [] {}, LamWatch{nullptr, 0, nullptr});
 }
 
 // Reset of the current copy (at plan time, for both copies).
@@ -1191,6 +1471,8 @@ __global__ void graph_setup_kernel(ChainArgs a, GraphDims g) {
         if (q == 0) {
             a.ctl[kCtlStatus] = 0;
             a.nxt_ctl[kCtlStatus] = 0;
+            a.ctl[kCtlRereads] = 0;
+            a.nxt_ctl[kCtlRereads] = 0;
         }
     }
 }
@@ -1207,11 +1489,11 @@ __global__ void poison_kernel(uint32_t *p, size_t words, uint32_t pattern) {
 // ----------------------------------------------------------------------------
 // Workgroups of this instantiation the current device holds at once (its
 // occupancy times the compute units), computed once per process.
-template <class Body, bool SPLIT>
+template <class Body, bool SPLIT, bool LAM>
 int resident_capacity() {
     static const int cap = [] {
         int occ = 0, dev = 0, cus = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, worker_kernel<Body, SPLIT>, Body::NT, 0) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, worker_fn<Body, SPLIT, LAM>(), Body::NT, 0) !=
                 hipSuccess ||
             hipGetDevice(&dev) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -1224,26 +1506,34 @@ int resident_capacity() {
 // The queue protocol's forward progress needs every worker resident, so a
 // grid larger than the launched instantiation's capacity is refused
 // (hipErrorCooperativeLaunchTooLarge) instead of launched.
-template <class Body, bool SPLIT>
+template <class Body, bool SPLIT, bool LAM>
 hipError_t launch_worker_s(const ChainArgs &a, int grid, bool cooperative, hipStream_t s) {
-    if (grid > resident_capacity<Body, SPLIT>()) return hipErrorCooperativeLaunchTooLarge;
+    if (grid > resident_capacity<Body, SPLIT, LAM>()) return hipErrorCooperativeLaunchTooLarge;
     if (!cooperative) {
-        hipLaunchKernelGGL((worker_kernel<Body, SPLIT>), dim3(grid), dim3(Body::NT), 0, s, a);
+        hipLaunchKernelGGL((worker_fn<Body, SPLIT, LAM>()), dim3(grid), dim3(Body::NT), 0, s, a);
         return hipGetLastError();
     }
     ChainArgs copy = a;
     void *args[] = {&copy};
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(worker_kernel<Body, SPLIT>), dim3(grid),
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(worker_fn<Body, SPLIT, LAM>()), dim3(grid),
                                       dim3(Body::NT), args, 0, s);
 }
 
-// A plan with a split layer launches the split-K instantiation.
+// A plan with a split layer launches the split-K instantiation, a Lamport
+// plan the Lamport one.
 template <class Body>
 hipError_t launch_worker_t(const ChainArgs &a, int grid, bool cooperative, hipStream_t s) {
-    bool split = false;
-    for (int l = 0; l < a.L; ++l) split |= a.layer[l].nsplit > 1;
-    if (split) return launch_worker_s<Body, true>(a, grid, cooperative, s);
-    return launch_worker_s<Body, false>(a, grid, cooperative, s);
+    bool split = false, lam = false;
+    for (int l = 0; l < a.L; ++l) {
+        split |= a.layer[l].nsplit > 1;
+        lam |= a.layer[l].lam_in != 0;
+    }
+    if (lam) {
+        if (split) return launch_worker_s<Body, true, true>(a, grid, cooperative, s);
+        return launch_worker_s<Body, false, true>(a, grid, cooperative, s);
+    }
+    if (split) return launch_worker_s<Body, true, false>(a, grid, cooperative, s);
+    return launch_worker_s<Body, false, false>(a, grid, cooperative, s);
 }
 
 template <class Body>
@@ -1261,15 +1551,20 @@ hipError_t launch_layer_t(const ChainArgs &a, int l, int rb0, int nrb, hipStream
 // Workgroups of the persistent worker one compute unit holds at once.  A
 // plan sizes its grid before it knows whether it will launch the split-K
 // instantiation, whose register use differs, so this is the smaller of the
-// two instantiations' figures: every worker of either is then resident,
-// which the queue protocol's forward progress relies on.
+// two instantiations' figures (Lamport plans: of the two Lamport ones):
+// every worker of either is then resident, which the queue protocol's
+// forward progress relies on.
 template <class Body>
-hipError_t occupancy_t(int *blocks) {
-    int plain = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&plain, worker_kernel<Body, false>, Body::NT, 0);
+hipError_t occupancy_t(int *blocks, bool lamport) {
+    int plain = 0, split = 0;
+    hipError_t e = lamport
+                       ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&plain, worker_fn<Body, false, true>(),
+                                                                      Body::NT, 0)
+                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&plain, worker_fn<Body, false, false>(),
+                                                                      Body::NT, 0);
     if (e != hipSuccess) return e;
-    int split = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&split, worker_kernel<Body, true>, Body::NT, 0);
+    e = lamport ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&split, worker_fn<Body, true, true>(), Body::NT, 0)
+                : hipOccupancyMaxActiveBlocksPerMultiprocessor(&split, worker_fn<Body, true, false>(), Body::NT, 0);
     if (e != hipSuccess) return e;
     *blocks = split < plain ? split : plain;
     return hipSuccess;
@@ -1430,6 +1725,26 @@ hipError_t launch_graph_setup(const ChainArgs &a, const GraphDims &g, hipStream_
     if (grid > 1024) grid = 1024;
     if (grid < 1) grid = 1;
     hipLaunchKernelGGL(graph_setup_kernel, dim3(grid), dim3(kThreads), 0, s, a, g);
+    return hipGetLastError();
+}
+
+// Sentinel fill of a Lamport intermediate, written through to memory.
+__global__ void fill_kernel(uint64_t *p, size_t n16, uint32_t pattern) {
+    const uint64_t pat = (uint64_t)pattern | ((uint64_t)pattern << 32);
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x; c < n16; c += stride) {
+        __hip_atomic_store(p + 2 * c, pat, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(p + 2 * c + 1, pat, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+hipError_t launch_fill(void *p, size_t bytes, uint32_t pattern, hipStream_t s) {
+    const size_t n16 = bytes / 16;
+    if (n16 == 0) return hipSuccess;
+    size_t grid = (n16 + kThreads - 1) / kThreads;
+    if (grid > 2048) grid = 2048;
+    hipLaunchKernelGGL(fill_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, static_cast<uint64_t *>(p), n16,
+                       pattern);
     return hipGetLastError();
 }
 

@@ -32,6 +32,7 @@ CP_FLAG_COOPERATIVE = 64
 CP_FLAG_FENCE_RELEASE = 128
 CP_FLAG_TIMING = 256
 CP_FLAG_NO_SPLIT = 512
+CP_FLAG_LAMPORT = 1024
 CP_MAX_LAYERS = 8
 
 # every symbol include/cp_chain.h declares
@@ -50,7 +51,8 @@ class cp_chain_stats_t(ctypes.Structure):
         ("n_queues", ctypes.c_int32), ("queues_drained", ctypes.c_int32),
         ("order_violations", ctypes.c_int32), ("last_run_ms", ctypes.c_double),
         ("last_kernel_ms", ctypes.c_double), ("nonzero_arrivals", ctypes.c_int32),
-        ("nsplit", ctypes.c_int32 * 8), ("fenced", ctypes.c_int32),
+        ("nsplit", ctypes.c_int32 * 8), ("fenced", ctypes.c_int32), ("lamport", ctypes.c_int32),
+        ("lamport_rereads", ctypes.c_int32),
     ]
 
     def as_dict(self):
