@@ -230,17 +230,20 @@ int cp_chain_stats(cp_chain *plan, cp_chain_stats_t *out);
 
 /*
  * cp_chain_trace -- copy the per-tile timestamps of the last pipelined run
- * (plan built with CP_FLAG_TRACE) into host memory `out` of 6*T uint64
+ * (plan built with CP_FLAG_TRACE) into host memory `out` of 8*T uint64
  * (CP_TRACE_WORDS per tile, tile-ID order):
  *   [0..3] ticket taken, tile dequeued (ready), GEMM body done, stores
  *          released, in 100 MHz wall-clock ticks -- the epilogue /
  *          visibility / prologue phases of the paper's Fig. 2;
  *   [4..5] the shader clock counter (s_memtime) at dequeue and at body done,
  *          so (w[5] - w[4]) / (w[2] - w[1]) x 100 MHz is the clock the tile's
- *          compute unit ran at (under a power cap it differs between XCDs).
- * CP_ERR_INVALID_ARG without the flag or with capacity < 6*T.
+ *          compute unit ran at (under a power cap it differs between XCDs);
+ *   [6]    the persistent workgroup that ran the tile;
+ *   [7]    1 if its release was deferred until the same worker's next tile
+ *          had requested its first slabs (that tile was already queued).
+ * CP_ERR_INVALID_ARG without the flag or with capacity < 8*T.
  */
-#define CP_TRACE_WORDS 6
+#define CP_TRACE_WORDS 8
 int cp_chain_trace(cp_chain *plan, uint64_t *out, int64_t capacity);
 
 /*

@@ -341,6 +341,35 @@ def test_many_tiles_many_waves(rt):
     assert same_bits(out["pipelined"], out["sequential"])
 
 
+@pytest.mark.parametrize("dtype", [gen.F32, gen.BF16], ids=["f32", "bf16"])
+def test_deferred_release_exact(rt, dtype):
+    """More first-layer tiles than workers: a worker whose next slot is
+    already filled when its tile ends releases that tile only after the next
+    one has requested its first slabs (the trace marks those).  Deferred
+    releases must occur, no consumer may start before any of its producers
+    released (the trace order check), and the signed-permutation chain stays
+    exact with NaN-poisoned intermediates and delayed producers."""
+    f = rt_flags()
+    M, n = 8192, 512
+    tile = (64, 64)
+    X = gen.normal_matrix((M, n), 1.0, 180, dtype)
+    Ws = [gen.signed_permutation(n, 181 + l, dtype, scale_pow2=s) for l, s in enumerate((1, 0, -1))]
+    torch, ch, nat = rt["torch"], rt["chain"], rt["nat"]
+    dX, dW = ch.to_device(X, dtype), [ch.to_device(w, dtype) for w in Ws]
+    ref = oracle.chain(X, Ws, dtype)
+    with ch.Chain(M, [n] * 4, dtype, tile[0], tile[1], flags=all_flags() | f["DELAY"]) as c:
+        for rep in range(2):
+            dY = torch.full((M, n), float("nan"), dtype=ch.DTYPES[dtype], device="cuda")
+            c.run(dX, dW, dY)
+            st = c.stats()
+            check_invariants(st, all_flags())
+            tr = np.array(c.trace(), dtype=np.uint64).reshape(-1, nat.CP_TRACE_WORDS).astype(np.int64)
+            deferred = int(tr[:, 7].sum())
+            say("deferred releases", deferred, "of", st["n_tiles"], "tiles;", st["n_workers"], "workers")
+            assert deferred > 0
+            assert np.array_equal(as_values(ch.to_host(dY, dtype), dtype), ref)
+
+
 def test_trace_stamps(rt):
     """The trace holds, per tile, wall-clock stamps in protocol order (ticket
     taken <= dequeued <= body done <= released) and shader-clock stamps
@@ -358,7 +387,8 @@ def test_trace_stamps(rt):
         tr = np.array(c.trace(), dtype=np.uint64).reshape(-1, nat.CP_TRACE_WORDS).astype(np.int64)
     T = st["n_tiles"]
     first_layer = (M // 128) * (widths[1] // 128)
-    assert tr.shape == (T, 6)
+    assert tr.shape == (T, 8)
+    assert tr[:, 6].max() < st["n_workers"] and set(np.unique(tr[:, 7])) <= {0, 1}
     assert (tr[:, 0] <= tr[:, 1]).all() and (tr[:, 1] < tr[:, 2]).all()
     assert (tr[:first_layer, 3] >= tr[:first_layer, 2]).all()   # producers released after their body
     assert (tr[first_layer:, 3] == 0).all()                       # last layer releases nothing

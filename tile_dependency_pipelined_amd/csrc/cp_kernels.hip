@@ -284,10 +284,13 @@ struct Bf16Body {
     // copy alone, so the product never sees a sentinel and the result is
     // the same bits as in every other mode.  `before_store` runs in every
     // thread right before the tile's global stores.
-    template <bool SPLIT, bool LAM, class Hook, class StoreHook>
+    // `after_issue` runs in every thread once the tile's first slabs are
+    // requested, while they are in flight (the worker releases a previous
+    // tile there).
+    template <bool SPLIT, bool LAM, class Hook, class StoreHook, class IssueHook>
     __device__ __forceinline__ static bool run(const LayerDesc &d, int i, int j, int split, uint32_t *arrive,
                                                char *const *stg, Hook &&before_epilogue, StoreHook &&before_store,
-                                               const LamWatch &lw) {
+                                               IssueHook &&after_issue, const LamWatch &lw) {
         const uint16_t *__restrict__ A = static_cast<const uint16_t *>(d.A);
         const uint16_t *__restrict__ W = static_cast<const uint16_t *>(d.W);
         uint16_t *__restrict__ C = static_cast<uint16_t *>(d.C);
@@ -546,6 +549,7 @@ struct Bf16Body {
         };
 #pragma unroll
         for (int u = 0; u < S; ++u) issue(stg[u], (u < nk ? u : nk - 1) * BK);
+        after_issue();
         wait_vmcnt<(S - 1) * PER>();
         mark(stg[0], 0);
         __syncthreads();
@@ -800,10 +804,10 @@ struct F32Body {
     // LAM: the A values of every slab are checked for the sentinel -0.0 when
     // they move from registers to LDS and re-read from memory until they
     // hold none (see Bf16Body); `before_store` as in Bf16Body.
-    template <bool SPLIT, bool LAM, class Hook, class StoreHook>
+    template <bool SPLIT, bool LAM, class Hook, class StoreHook, class IssueHook>
     __device__ __forceinline__ static bool run(const LayerDesc &d, int i, int j, int split, uint32_t *arrive,
                                                char *const *stg, Hook &&before_epilogue, StoreHook &&before_store,
-                                               const LamWatch &lw) {
+                                               IssueHook &&after_issue, const LamWatch &lw) {
         const int K = d.K, N = d.N;
         const int kspan = SPLIT ? __builtin_amdgcn_readfirstlane(K / d.nsplit) : K;
         const int kbeg = SPLIT ? __builtin_amdgcn_readfirstlane(split * kspan) : 0;
@@ -896,6 +900,7 @@ struct F32Body {
         const int nk = kspan / BK;
         // slabs past the last one re-load the last slab (in bounds, unused)
         gload(0, r0);
+        after_issue();  // with one slab in registers, not four
         gload((1 < nk ? 1 : nk - 1) * BK, r1);
         gload((2 < nk ? 2 : nk - 1) * BK, r2);
         gload((3 < nk ? 3 : nk - 1) * BK, r3);
@@ -1094,6 +1099,7 @@ __device__ __forceinline__ void dequeued(const ChainArgs &a, uint32_t id, uint64
         a.trace[kTraceWords * (size_t)id + 0] = t0;
         a.trace[kTraceWords * (size_t)id + 1] = wall_clock64();
         a.trace[kTraceWords * (size_t)id + 4] = clock64();
+        a.trace[kTraceWords * (size_t)id + 6] = blockIdx.x;
     }
 }
 
@@ -1153,13 +1159,19 @@ __device__ __forceinline__ uint32_t first_slot(const ChainArgs &a, int q, uint32
 // their owner queues, one tail atomic per queue.
 //   Lamport (the tile's layer has lam_out): no wait at all; consumers check
 //     the data itself for the sentinel and re-read it until it has landed.
-__device__ __forceinline__ void publish(const ChainArgs &a, uint32_t id, int l) {
+//
+// release_stores: every thread, once its stores are issued (the completion
+// wait and the barrier); publish_edges: wave 0 only, any time after it (the
+// fence, the decrements and the pushes); publish: both at once.
+__device__ __forceinline__ void release_stores(const ChainArgs &a, int l) {
     const bool fenced = (a.flags & CP_FLAG_FENCE_RELEASE) != 0;
     if (!fenced && !a.layer[l].lam_out) wait_vmcnt<0>();
     __syncthreads();
-    const int tid = threadIdx.x;
-    if (tid >= 64) return;
-    const int lane = tid;
+}
+
+__device__ __forceinline__ void publish_edges(const ChainArgs &a, uint32_t id, int l) {
+    const bool fenced = (a.flags & CP_FLAG_FENCE_RELEASE) != 0;
+    const int lane = threadIdx.x & 63;
     if (fenced) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     if ((a.flags & CP_FLAG_DELAY_INJECT) && ((id * 2654435761u) >> 30) == 0) {
         const uint64_t s = wall_clock64();
@@ -1201,6 +1213,11 @@ __device__ __forceinline__ void publish(const ChainArgs &a, uint32_t id, int l) 
             __hip_atomic_store(a.queue + a.qbase[cq] + base + rank, c, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     }
+}
+
+__device__ __forceinline__ void publish(const ChainArgs &a, uint32_t id, int l) {
+    release_stores(a, l);
+    if (threadIdx.x < 64) publish_edges(a, id, l);
 }
 
 __device__ __forceinline__ void decode(const ChainArgs &a, uint32_t id, int &l, int &i, int &j, int &split) {
@@ -1249,9 +1266,10 @@ __device__ __forceinline__ void reset_copy(const ChainArgs &a, uint32_t *queue, 
     }
 }
 
-// Lane 0 of wave 1: the worker's scheduler (takes tickets, polls slots),
-// while wave 0 is the publisher.
-constexpr int kSchedLane = 64;
+// Lane 0 of wave 0: the worker's scheduler (takes tickets, peeks and polls
+// slots).  Wave 0 is also the publisher, so the wave that knows whether the
+// next tile is already there is the one that decides when to release.
+constexpr int kSchedLane = 0;
 
 // Lamport plans: this worker's share of the sentinel fill of the other copy
 // of the intermediates (used by the next run), 16-byte stores written
@@ -1300,6 +1318,26 @@ __device__ __forceinline__ void worker_loop(ChainArgs &a) {
     bool first = true;
     bool filled = !LAM;
     const LamWatch lw{a.ctl + kCtlStatus, a.timeout_ticks, a.deq_count ? a.ctl + kCtlRereads : nullptr};
+    // Deferred release (wave roles, Fig. 2(b)): when the scheduler lane finds
+    // its next slot already filled as the tile body ends, wave 0 does not
+    // release the finished tile before the next one starts; it does so once
+    // the next tile's first slabs are requested, while they are in flight.
+    // The MFMA waves thus start the next tile without waiting for the
+    // decrements and pushes.  Only a tile that is already there (its inputs
+    // complete) is started before the release, so no wait can depend on the
+    // deferred release.
+    uint32_t pending = kEmpty;  // deferred tile (wave 0's view; uniform in wave 0)
+    int pending_l = 0;
+    uint32_t peek = 0;          // scheduler lane: the next slot held a tile
+    // wave 0 by a wave-uniform test, so that the deferral state stays in
+    // scalar registers
+    const bool wave0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0;
+    auto release_pending = [&] {
+        if (wave0 && pending != kEmpty) {
+            publish_edges(a, pending, pending_l);
+            pending = kEmpty;
+        }
+    };
     if (LAM && threadIdx.x < 4) lamport_flags()[threadIdx.x] = 0u;  // before the loop's first barrier
     for (;;) {
         if (sched) *slot = first ? first_slot(a, q, ticket) : wait_slot(a, q, ticket);
@@ -1315,8 +1353,13 @@ __device__ __forceinline__ void worker_loop(ChainArgs &a) {
         const uint32_t first_item_id = id - (uint32_t)split;  // the tile's first item carries its edges
         bool released = false;
         auto next_ticket = [&] {
-            if (sched) ticket = take_ticket(a, q);
+            if (sched) {
+                ticket = take_ticket(a, q);
+                // the load's round trip overlaps the epilogue
+                peek = ticket < (uint32_t)a.qsize[q] ? (ld_relaxed(a.queue + a.qbase[q] + ticket) != kEmpty) : 0u;
+            }
         };
+
         auto store_hook = [&] {
             if constexpr (LAM) {
                 if ((a.flags & CP_FLAG_DELAY_INJECT) && l + 1 < a.L && ((first_item_id * 2654435761u) >> 30) == 0) {
@@ -1333,24 +1376,37 @@ __device__ __forceinline__ void worker_loop(ChainArgs &a) {
         bool done;
         if (LAM && a.layer[l].lam_in)
             done = Body::template run<SPLIT, true>(a.layer[l], i, j, split, a.arrive + first_item_id, stg, next_ticket,
-                                                   store_hook, lw);
+                                                   store_hook, release_pending, lw);
         else
             done = Body::template run<SPLIT, false>(a.layer[l], i, j, split, a.arrive + first_item_id, stg,
-                                                    next_ticket, store_hook, lw);
+                                                    next_ticket, store_hook, release_pending, lw);
         if (a.trace && threadIdx.x == 0) {
             a.trace[kTraceWords * (size_t)id + 2] = wall_clock64();
             a.trace[kTraceWords * (size_t)id + 5] = clock64();
         }
-        // after publish's opening barrier wave 0 releases the tile while the
-        // scheduler lane (wave 1) already waits for the next one; a split-K
-        // item that did not complete its tile has nothing to release
-        if (done && l + 1 < a.L && !released) publish(a, first_item_id, l);
-        else __syncthreads();
+        // a split-K item that did not complete its tile has nothing to
+        // release; a completed one is released now, or, if the next tile is
+        // already there, right after that tile's first loads are requested
+        if (done && l + 1 < a.L && !released) {
+            release_stores(a, l);
+            if (wave0) {
+                if (__builtin_amdgcn_readfirstlane(peek)) {
+                    pending = first_item_id;
+                    pending_l = l;
+                    if (a.trace && threadIdx.x == 0) a.trace[kTraceWords * (size_t)first_item_id + 7] = 1;
+                } else {
+                    publish_edges(a, first_item_id, l);
+                }
+            }
+        } else {
+            __syncthreads();
+        }
         if (LAM && !filled) {
             filled = true;
             lamport_fill_share(a, Body::NT);
         }
     }
+    release_pending();  // (never pending here: a deferred release always has a next tile)
     if (LAM && !filled) lamport_fill_share(a, Body::NT);  // a worker that got no tile
     // Reset the other copy of the per-run state for the next run: nothing of
     // this run reads it, and the kernel boundary publishes it.  Done on the
@@ -1399,7 +1455,7 @@ __global__ void __launch_bounds__(Body::NT) layer_kernel(ChainArgs a, int l, int
     const int i = __builtin_amdgcn_readfirstlane(rb0 + t / per_rb), rem = t % per_rb;
     const int j = __builtin_amdgcn_readfirstlane(rem / d.nsplit), split = __builtin_amdgcn_readfirstlane(rem % d.nsplit);
     (void)Body::template run<SPLIT, false>(d, i, j, split, a.arrive + d.tile_off + (i * d.nbn + j) * d.nsplit,
-                                           stg, [] {}, [] {}, LamWatch{nullptr, 0, nullptr});
+                                           stg, [] {}, [] {}, [] {}, LamWatch{nullptr, 0, nullptr});
 }
 
 // Reset of the current copy (at plan time, for both copies).

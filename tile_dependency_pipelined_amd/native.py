@@ -167,7 +167,7 @@ def cp_chain_stats(plan, check=True):
     return d
 
 
-CP_TRACE_WORDS = 6
+CP_TRACE_WORDS = 8
 
 
 def cp_chain_trace(plan, n_tiles):
