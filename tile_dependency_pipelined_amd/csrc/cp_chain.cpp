@@ -566,7 +566,12 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
         std::vector<int32_t> size(lx.nq, 0);
         for (int l = 0; l < n_layers; ++l)
             for (int32_t t = g.layer_off[l]; t < g.layer_off[l + 1]; ++t) {
-                const int q = ((t - g.layer_off[l]) % (g.nbn[l] * g.nsplit[l])) % lx.nq;
+                cp::LayerDesc d;
+                memset(&d, 0, sizeof d);
+                d.tile_off = g.layer_off[l];
+                d.nbn = g.nbn[l];
+                d.nsplit = g.nsplit[l];
+                const int q = cp::owner_queue(d, t, lx.nq);
                 ++size[q];
                 if (l == 0) first[q].push_back((uint32_t)t);  // row-block-major (then item order)
             }
