@@ -158,6 +158,23 @@ def summarize(args):
             wk = counter_per_dispatch(rows, lambda n: WORKER in n, counter)
             if wk:
                 kv[f"pmc_{counter}_per_launch"] = f"{statistics.median(wk.values()):.6g}"
+    # derived figures (each counter is the worker kernel's median per dispatch;
+    # SQ cycle counters of a wave count 4-cycle units, the CU ones cycles)
+    def pmc(name):
+        v = kv.get(f"pmc_{name}_per_launch")
+        return float(v) if v is not None else None
+    hit, miss = pmc("TCC_HIT_sum"), pmc("TCC_MISS_sum")
+    if hit is not None and miss is not None and hit + miss > 0:
+        kv["derived_l2_hit_rate"] = f"{hit / (hit + miss):.3f}"
+    busy, cu = pmc("SQ_VALU_MFMA_BUSY_CYCLES"), pmc("SQ_BUSY_CU_CYCLES")
+    if busy is not None and cu:
+        kv["derived_mfma_busy_frac_per_simd"] = f"{busy / (4 * cu):.3f}"
+    wait, wave = pmc("SQ_WAIT_ANY"), pmc("SQ_WAVE_CYCLES")
+    if wait is not None and wave:
+        kv["derived_wave_wait_frac"] = f"{wait / wave:.3f}"
+    lds_wait = pmc("SQ_WAIT_INST_LDS")
+    if lds_wait is not None and wave:
+        kv["derived_wave_lds_issue_wait_frac"] = f"{lds_wait / wave:.3f}"
     if "fetch_bytes_per_launch" in kv and "write_bytes_per_launch" in kv:
         kv["hbm_bytes_per_launch"] = str(int(float(kv["fetch_bytes_per_launch"]) +
                                              float(kv["write_bytes_per_launch"])))
