@@ -108,9 +108,46 @@ __device__ __forceinline__ void lamport_reread(const uint64_t *src, uint64_t (&v
     }
 }
 
+// A pointer every lane holds the same value of, in scalar registers (an
+// out-of-line function receives its arguments in vector registers).  The
+// builtin returns a signed int: each half goes through uint32_t before it is
+// widened, or a low half with bit 31 set would fill the high half with ones.
+template <class T>
+__device__ __forceinline__ T *uniform_ptr(T *p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<T *>(((uint64_t)hi << 32) | lo);
+}
+
 // Fourth word of a raw (stride 0) buffer resource on gfx9-family parts:
 // 32-bit data format, so untyped dword loads are in range.
 constexpr int kRsrcWord3 = 0x00020000;
+
+// 16-byte direct load (buffer_load_dwordx4 ... lds): each lane's 16 bytes at
+// byte `voff` of the resource go to LDS at `lds` + 16 * lane (`lds`
+// wave-uniform).  Inline asm, so that the compiler's wait insertion does not
+// track it: the compiler cannot tell which LDS array a direct load writes,
+// and before every later LDS read it waits for ALL direct loads in flight,
+// which leaves a multi-stage pipeline one slab in flight.  Every read of
+// data loaded this way therefore follows an explicit wait_vmcnt (and a
+// barrier where other waves loaded it).  The asm writes no VGPR (the data
+// goes to LDS) and restores M0, which the compiler does not let an asm
+// clobber; the compiler's own waits for its loads only get stricter, since
+// these count in vmcnt too.  The memory clobber keeps LDS reads on their
+// side of it (the compiler does not otherwise know that it writes LDS).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, const void *lds, uint32_t voff) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(const lds_void_t *)lds);
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(m0), "v"(voff), "s"(r)
+        : "memory");
+}
 
 // Four LDS words of a Lamport consumer: flags of the last three slabs'
 // checks and of a re-load round (zeroed at worker start and after each tile).
@@ -155,9 +192,10 @@ __device__ __forceinline__ uint32_t *lamport_flags() {
 // Pipeline: S-1 slabs are in flight while one is multiplied; a stage is
 // refilled as soon as every wave holds the fragments of its last k step.
 // Every stage is its own __shared__ array and every stage index a
-// compile-time constant, so the compiler can tell that loads in flight into
-// one stage do not alias reads of another and does not wait for them before
-// reading.  Past the last slab the prefetch re-reads the last slab into a
+// compile-time constant (no dynamic LDS addressing).  With more than two
+// stages the direct loads are hidden from the compiler's wait insertion
+// (dma16), so the explicit waits below alone decide how many slabs stay in
+// flight.  Past the last slab the prefetch re-reads the last slab into a
 // stage that is no longer read, which keeps the number of loads in flight,
 // and so the wait, constant.
 // ----------------------------------------------------------------------------
@@ -185,6 +223,14 @@ struct Bf16Body {
     static constexpr int B_PW = B_BYTES / 1024 / NW;  // (W)
     static constexpr int PER = A_PW + B_PW;          // loads per wave per slab
     static constexpr int STAGE = A_BYTES + B_BYTES;  // bytes of one LDS stage
+    // Direct loads through dma16 where more than one slab is meant to be in
+    // flight; with one (two stages) the compiler's own waits are the
+    // pipeline's, and the builtin leaves it more freedom to schedule.
+    static constexpr bool ASM_DMA = S > 2;
+    __device__ __forceinline__ static void dma(__amdgpu_buffer_rsrc_t r, char *lds, uint32_t voff) {
+        if constexpr (ASM_DMA) dma16(r, lds, voff);
+        else __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t *)lds, 16, voff, 0, 0, 0);
+    }
     static_assert(BM >= 64 && BN >= 64 && BM <= 256 && BN <= 256, "tile");
     static_assert(MI == 32 || MI == 16, "MFMA block");
     static_assert(WM >= 32 && WN >= 32 && WM % 32 == 0 && WN % 32 == 0, "wave sub-tile");
@@ -241,11 +287,10 @@ struct Bf16Body {
             __syncthreads();  // every wave has read the flags
             if (tid == 0) lflag[3] = 0u;
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(src, 0, (int)bytes, kRsrcWord3);
+            const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+                uniform_ptr(src), 0, (int)__builtin_amdgcn_readfirstlane(bytes), kRsrcWord3);
 #pragma unroll
-            for (int q = 0; q < A_PW; ++q)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t *)(As + (q * NW + wave) * 1024), 16, a_off.v[q],
-                                                         0, 0, 0);
+            for (int q = 0; q < A_PW; ++q) dma(ra, As + (q * NW + wave) * 1024, a_off.v[q]);
             wait_vmcnt<0>();
             __syncthreads();  // lflag[3] cleared before any wave marks it
             uint32_t bad = 0;
@@ -358,15 +403,11 @@ struct Bf16Body {
             const __amdgpu_buffer_rsrc_t ra =
                 __builtin_amdgcn_make_buffer_rsrc(a_base + (size_t)k0 * 2, 0, (int)(a_bytes - 2u * k0), kRsrcWord3);
 #pragma unroll
-            for (int q = 0; q < A_PW; ++q)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t *)(As + (q * NW + wave) * 1024), 16,
-                                                         a_off[q], 0, 0, 0);
+            for (int q = 0; q < A_PW; ++q) dma(ra, As + (q * NW + wave) * 1024, a_off[q]);
             const __amdgpu_buffer_rsrc_t rw =
                 __builtin_amdgcn_make_buffer_rsrc(w_base + (size_t)k0 * N * 2, 0, (int)w_bytes, kRsrcWord3);
 #pragma unroll
-            for (int q = 0; q < B_PW; ++q)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t *)(Bs + (q * NW + wave) * 1024), 16,
-                                                         b_off[q], 0, 0, 0);
+            for (int q = 0; q < B_PW; ++q) dma(rw, Bs + (q * NW + wave) * 1024, b_off[q]);
         };
 
         // fragment addresses that do not depend on the stage or k step
@@ -713,14 +754,17 @@ struct Bf16Body {
         constexpr int RPS0 = STAGE / (BN * 2);     // tile rows one stage holds
         constexpr int RPS = RPS0 >= BM ? BM : RPS0;  // tile rows per stage used
         constexpr int UPR = BN / 4;                // 8-byte units per row
-        static_assert(RPS % 32 == 0 && RPS * S >= BM && NT % UPR == 0 && RPS % (NT / UPR) == 0,
+        constexpr int NUSE = (BM + RPS - 1) / RPS;  // stages the tile needs
+        static_assert(RPS % 32 == 0 && NUSE <= S && NT % UPR == 0 && RPS % (NT / UPR) == 0,
                       "epilogue staging");
-        auto stage_of = [&](int k) -> char * {     // k uniform; no dynamic array indexing
+        // k uniform; selects among the stages the tile needs only (a select
+        // over more of them became an indexed array in private memory)
+        auto stage_of = [&](int k) -> char * {
             char *p = stg[0];
-            if constexpr (S > 1) p = k == 1 ? stg[1] : p;
-            if constexpr (S > 2) p = k == 2 ? stg[2] : p;
-            if constexpr (S > 3) p = k == 3 ? stg[3] : p;
-            if constexpr (S > 4) p = k == 4 ? stg[4] : p;
+            if constexpr (NUSE > 1) p = k == 1 ? stg[1] : p;
+            if constexpr (NUSE > 2) p = k == 2 ? stg[2] : p;
+            if constexpr (NUSE > 3) p = k == 3 ? stg[3] : p;
+            if constexpr (NUSE > 4) p = k == 4 ? stg[4] : p;
             return p;
         };
         const int act = dp->act;
