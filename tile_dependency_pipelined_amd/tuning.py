@@ -4,8 +4,10 @@ check exactly the configuration that is timed."""
 
 # (tile_m, tile_n) per workload key of inputs.CONFIGS, chosen by the
 # pipelined time of each candidate, interleaved on one MI355X (microseconds):
-#   C2: 128x64 59-63; 64x128 60-61; 128x128 72; 64x64 75; 64x256 75;
-#       256x64 81; 256x128 98; 128x256 99; 256x256 115
+#   C2: 64x128 (four stages, one workgroup per CU, unsplit) 55-57;
+#       128x64 (three stages, two per CU, split 2) 59-61; 64x128 on three
+#       stages 61; 64x128 on four stages split 2 78; 128x128 72-77; 64x64
+#       64-75; 64x256 75; 256x64 81; 256x128 98; 128x256 99; 256x256 115
 #   C3: 256x256 395-428; 256x128 517; 128x256 521
 #   C4: 128x128 514-524; 256x128 525-545 (16x16x32 blocks, 8 waves: 554-560);
 #       256x256 539-547 (split 2; 516-525 with the pipelined split-K sum,
@@ -13,7 +15,7 @@ check exactly the configuration that is timed."""
 #   C5: 128x128 303-313; 256x64 376; 64x256 381; 128x256 407; 256x128 416
 TILES = {
     "c1": (64, 64),
-    "c2": (128, 64),
+    "c2": (64, 128),
     "c3": (256, 256),
     "c4": (128, 128),
     "c5": (128, 128),
