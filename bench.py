@@ -222,16 +222,24 @@ def main():
         # copies are laid out for one queue layout at a time, and a pipelined
         # run after a spatial run on the same plan would first re-lay one
         # out (an extra reset launch inside its timed span)
-        # the Lamport-sentinel release is a plan of its own too
+        # the Lamport-sentinel release is a plan of its own too; the
+        # micro-batched baseline needs at least two row chunks, and where the
+        # timed tile spans the whole batch it runs on a plan of lower tiles
+        mb_tile = tuning.microbatch_tile(cfg.M, tile)
         with ch.Chain(cfg.M, cfg.widths, cfg.dtype, tile[0], tile[1], acts=list(cfg.acts)) as sp, \
                 ch.Chain(cfg.M, cfg.widths, cfg.dtype, tile[0], tile[1], acts=list(cfg.acts),
-                         flags=nat.CP_FLAG_LAMPORT) as lp:
+                         flags=nat.CP_FLAG_LAMPORT) as lp, \
+                ch.Chain(cfg.M, cfg.widths, cfg.dtype, mb_tile[0], mb_tile[1], acts=list(cfg.acts)) as mp:
             def step_modes(mode="pipelined", mb=0):
                 if mode == "lamport":
                     step("pipelined", 0, p=lp)
+                elif mode == "microbatch":
+                    step(mode, mb, p=mp if mb_tile != tile else plan)
                 else:
                     step(mode, mb, p=sp if mode == "spatial" else plan)
-            result["modes"] = compare_modes(plan, step_modes, stream, cfg, tile, args.reps, torch, tuning)
+            result["modes"] = compare_modes(plan, step_modes, stream, cfg, mb_tile, args.reps, torch, tuning)
+            if mb_tile != tile:
+                result["modes"]["microbatch_tile"] = list(mb_tile)
 
     if not args.profile:
         result["gpu_state_after_timed_steps"] = gpu_state()
@@ -270,7 +278,7 @@ def roofline(flops, min_bytes, launch_ms, peak_tflops):
     return "hbm", min_bytes / (launch_ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s", intensity
 
 
-def compare_modes(plan, step, stream, cfg, tile, reps, torch, tuning):
+def compare_modes(plan, step, stream, cfg, mb_tile, reps, torch, tuning):
     """Latency of single runs of each mode, warm (back to back) and cold (a
     1 GiB device write before each run, outside the timed span).  The modes
     are interleaved, one run of each per round in a rotating order, so that
@@ -279,7 +287,7 @@ def compare_modes(plan, step, stream, cfg, tile, reps, torch, tuning):
     time out of the span.  Median, min, p10, p90 per mode."""
     scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
     runs = [("pipelined", 0), ("sequential", 0), ("spatial", 0), ("lamport", 0)]
-    runs += [("microbatch", m) for m in tuning.chunk_sweep(cfg.M, tile[0])]
+    runs += [("microbatch", m) for m in tuning.chunk_sweep(cfg.M, mb_tile[0])]
 
     def one(mode, mb, cold):
         if cold:

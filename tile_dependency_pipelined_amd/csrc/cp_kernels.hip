@@ -1702,15 +1702,20 @@ hipError_t occupancy_t(int *blocks, bool lamport) {
 #define CP_S_64x64 4
 #endif
 
-// wave grid (waves along M x along N) per tile shape
+// wave grid (waves along M x along N) per tile shape.  The one-workgroup-
+// per-CU shapes take 8 waves (two per SIMD, which cover each other's barrier
+// and LDS waits); 256x128 and 128x256 on 4 x 2 waves of 64 x 64 (or 32 x
+// 128): on 256 x 8192 x 28672 x 8192 with tanh-GeLU, 256x128 tiles ran the
+// pipelined chain in 280.3 us against 302.8 us for 128x128 tiles, 2 x 4
+// waves 286.5 us, 2 x 2 waves 319.8 us.
 #ifndef CP_W_256x256
 #define CP_W_256x256 2, 4
 #endif
 #ifndef CP_W_256x128
-#define CP_W_256x128 2, 2
+#define CP_W_256x128 4, 2
 #endif
 #ifndef CP_W_128x256
-#define CP_W_128x256 2, 2
+#define CP_W_128x256 4, 2
 #endif
 #ifndef CP_W_128x128
 #define CP_W_128x128 2, 2
