@@ -1672,8 +1672,8 @@ hipError_t occupancy_t(int *blocks, bool lamport) {
 
 // LDS stages per tile shape: as many as fit the occupancy each shape aims for
 // (64x128: four stages, one workgroup per CU; on 512 x 4096 x 4096 x 4096
-// its 256 tiles per layer then run unsplit, 55.3 us against 59.1 us for
-// 128x64 tiles on three stages, two per CU, split two ways)
+// its 256 tiles per layer then run unsplit, 55.3 us on 4 waves against
+// 59.1 us for 128x64 tiles on three stages, two per CU, split two ways)
 #ifndef CP_S_256x256
 #define CP_S_256x256 2
 #endif
@@ -1707,7 +1707,8 @@ hipError_t occupancy_t(int *blocks, bool lamport) {
 // and LDS waits); 256x128 and 128x256 on 4 x 2 waves of 64 x 64 (or 32 x
 // 128): on 256 x 8192 x 28672 x 8192 with tanh-GeLU, 256x128 tiles ran the
 // pipelined chain in 280.3 us against 302.8 us for 128x128 tiles, 2 x 4
-// waves 286.5 us, 2 x 2 waves 319.8 us.
+// waves 286.5 us, 2 x 2 waves 319.8 us.  64x128 on 2 x 4 waves of 32 x 32:
+// 512 x 4096 x 4096 x 4096 in 54.7 us against 58.4 us on 2 x 2 waves.
 #ifndef CP_W_256x256
 #define CP_W_256x256 2, 4
 #endif
@@ -1730,7 +1731,7 @@ hipError_t occupancy_t(int *blocks, bool lamport) {
 #define CP_W_128x64 2, 2
 #endif
 #ifndef CP_W_64x128
-#define CP_W_64x128 2, 2
+#define CP_W_64x128 2, 4
 #endif
 #ifndef CP_W_64x64
 #define CP_W_64x64 2, 2

@@ -4,7 +4,8 @@ check exactly the configuration that is timed."""
 
 # (tile_m, tile_n) per workload key of inputs.CONFIGS, chosen by the
 # pipelined time of each candidate, interleaved on one MI355X (microseconds):
-#   C2: 64x128 (four stages, one workgroup per CU, unsplit) 55-57;
+#   C2: 64x128 (four stages, 8 waves as 2 x 4, one workgroup per CU,
+#       unsplit) 54.7; the same on 4 waves 55-58;
 #       128x64 (three stages, two per CU, split 2) 59-61; 64x128 on three
 #       stages 61; 64x128 on four stages split 2 78; 128x128 72-77; 64x64
 #       64-75; 64x256 75; 256x64 81; 256x128 98; 128x256 99; 256x256 115
