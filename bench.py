@@ -229,10 +229,14 @@ def main():
         with ch.Chain(cfg.M, cfg.widths, cfg.dtype, tile[0], tile[1], acts=list(cfg.acts)) as sp, \
                 ch.Chain(cfg.M, cfg.widths, cfg.dtype, tile[0], tile[1], acts=list(cfg.acts),
                          flags=nat.CP_FLAG_LAMPORT) as lp, \
+                ch.Chain(cfg.M, cfg.widths, cfg.dtype, tile[0], tile[1], acts=list(cfg.acts),
+                         flags=nat.CP_FLAG_LAMPORT | nat.CP_FLAG_EARLY_DISPATCH) as lep, \
                 ch.Chain(cfg.M, cfg.widths, cfg.dtype, mb_tile[0], mb_tile[1], acts=list(cfg.acts)) as mp:
             def step_modes(mode="pipelined", mb=0):
                 if mode == "lamport":
                     step("pipelined", 0, p=lp)
+                elif mode == "lamport_early":
+                    step("pipelined", 0, p=lep)
                 elif mode == "microbatch":
                     step(mode, mb, p=mp if mb_tile != tile else plan)
                 else:
@@ -286,7 +290,7 @@ def compare_modes(plan, step, stream, cfg, mb_tile, reps, torch, tuning):
     alike; a short GPU sleep before the start event keeps host submission
     time out of the span.  Median, min, p10, p90 per mode."""
     scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-    runs = [("pipelined", 0), ("sequential", 0), ("spatial", 0), ("lamport", 0)]
+    runs = [("pipelined", 0), ("sequential", 0), ("spatial", 0), ("lamport", 0), ("lamport_early", 0)]
     runs += [("microbatch", m) for m in tuning.chunk_sweep(cfg.M, mb_tile[0])]
 
     def one(mode, mb, cold):
@@ -320,7 +324,7 @@ def compare_modes(plan, step, stream, cfg, mb_tile, reps, torch, tuning):
             k = rep % len(runs)
             for r in runs[k:] + runs[:k]:
                 ts[r].append(one(r[0], r[1], cold))
-        for name in ("pipelined", "sequential", "spatial", "lamport"):
+        for name in ("pipelined", "sequential", "spatial", "lamport", "lamport_early"):
             out[f"{name}_{tag}"] = summary(ts[(name, 0)])
         # paired differences: run r of pipelined against run r of the other
         # mode, both from the same round of the interleaved order
@@ -331,6 +335,7 @@ def compare_modes(plan, step, stream, cfg, mb_tile, reps, torch, tuning):
                     "pipelined_faster_in": f"{sum(x < 0 for x in d)} of {len(d)} rounds"}
         out[f"pipelined_minus_sequential_{tag}"] = paired(("sequential", 0))
         out[f"pipelined_minus_lamport_{tag}"] = paired(("lamport", 0))
+        out[f"pipelined_minus_lamport_early_{tag}"] = paired(("lamport_early", 0))
         mbs = [r for r in runs if r[0] == "microbatch"]
         if mbs:
             sw = {str(r[1]): summary(ts[r]) for r in mbs}

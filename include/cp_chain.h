@@ -118,6 +118,18 @@ typedef struct cp_chain cp_chain; /* opaque plan */
  * producers release their tile before storing it (stored ~20 us later), so
  * that consumers do read sentinels. */
 #define CP_FLAG_LAMPORT 1024u
+/* with CP_FLAG_LAMPORT only (CP_ERR_INVALID_ARG otherwise): a producer tile's
+ * consumers are queued as soon as every item of the tile has been dequeued,
+ * i.e. has started, instead of once it is stored (CTA-Pipelining §V-A: with
+ * the sentinel in the data, the consumer itself waits for each value; the
+ * dependency array of §III only has to say that the producer is running).
+ * A consumer then waits inside its k loop, slab by slab, for the sentinel
+ * to leave the A data it reads.  Deadlock-free for any worker count: an
+ * item is queued only when all its producers are on workers, and a running
+ * item waits only on running or finished items (first-layer items wait on
+ * nothing).  A wait longer than the watchdog ends the run with
+ * CP_ERR_TIMEOUT.  Y is bit for bit that of every other mode. */
+#define CP_FLAG_EARLY_DISPATCH 2048u
 
 #define CP_MAX_LAYERS 8
 

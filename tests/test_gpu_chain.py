@@ -194,14 +194,24 @@ def test_signed_permutation_chain_exact_with_poison(rt, dtype, release):
     assert np.array_equal(as_values(out["spatial"], dtype), ref)
 
 
+def lamport_flags(nat, early):
+    return nat.CP_FLAG_LAMPORT | (nat.CP_FLAG_EARLY_DISPATCH if early else 0)
+
+
+EARLY = pytest.mark.parametrize("early", [False, True], ids=["released", "early"])
+
+
+@EARLY
 @pytest.mark.parametrize("dtype", [gen.F32, gen.BF16], ids=["f32", "bf16"])
-def test_lamport_release_before_store_exact(rt, dtype):
+def test_lamport_release_before_store_exact(rt, dtype, early):
     """Lamport-sentinel release with a quarter of producers releasing their
     tile before storing it (stored ~20 us later): consumers do read the
-    sentinel and must re-read until the data lands.  The signed-permutation
-    chain is exact, so the result must equal the oracle bit for bit, in
-    three consecutive runs (alternating intermediate copies, each refilled
-    by the previous run's workers), and equal the sequential mode's."""
+    sentinel and must re-read until the data lands.  With early dispatch
+    every consumer is queued once its producers have started, so it waits
+    inside its k loop for their stores.  The signed-permutation chain is
+    exact, so the result must equal the oracle bit for bit, in three
+    consecutive runs (alternating intermediate copies, each refilled by the
+    previous run's workers), and equal the sequential mode's."""
     f = rt_flags()
     nat = rt["nat"]
     tile = (64, 64) if dtype == gen.F32 else (128, 128)
@@ -209,8 +219,8 @@ def test_lamport_release_before_store_exact(rt, dtype):
     M = 4 * tile[0]
     X = gen.normal_matrix((M, n), 1.0, 160, dtype)
     Ws = [gen.signed_permutation(n, 161 + l, dtype, scale_pow2=s) for l, s in enumerate((1, -2, 0))]
-    say("lamport perm chain", dtype, tile, M, n)
-    out, st = run_modes(rt, X, Ws, dtype, tile, flags=all_flags() | f["DELAY"] | nat.CP_FLAG_LAMPORT,
+    say("lamport perm chain", dtype, tile, M, n, "early" if early else "released")
+    out, st = run_modes(rt, X, Ws, dtype, tile, flags=all_flags() | f["DELAY"] | lamport_flags(nat, early),
                         modes=("pipelined", "sequential"), reps=3)
     assert st["lamport"] == 1 and st["fenced"] == 0, st
     say("  waves that re-read a sentinel fragment in the last run:", st["lamport_rereads"])
@@ -226,19 +236,21 @@ def test_lamport_release_before_store_exact(rt, dtype):
     ("bf16 64x128 four layers", gen.BF16, 256, (256, 512, 384, 640, 256), (64, 128), (0, 1, 0, 0)),
     ("fp32 64x64 split", gen.F32, 128, (512, 512, 512), (64, 64), (0, 0)),
 ], ids=lambda c: c[0])
-def test_lamport_parity(rt, case):
+@EARLY
+def test_lamport_parity(rt, case, early):
     """Lamport mode against the oracle on several bodies, split-K layers and
-    GeLU, with delayed (release-before-store) producers: within the bar,
-    bit-identical to the sequential mode, invariants exact, in repeated
-    runs."""
+    GeLU, with delayed (release-before-store) producers, with and without
+    early dispatch (whose split producer tiles count their items' starts on
+    the arrival counter): within the bar, bit-identical to the sequential
+    mode, invariants exact, in repeated runs."""
     f = rt_flags()
     nat = rt["nat"]
     name, dtype, M, widths, tile, acts = case
     L = len(widths) - 1
     X, Ws = gen.chain_inputs(M, widths, dtype, 1.0, tuple(1 / np.sqrt(w) for w in widths[:-1]), 170)
-    say("lamport parity", name)
+    say("lamport parity", name, "early" if early else "released")
     out, st = run_modes(rt, X, Ws, dtype, tile, acts=list(acts),
-                        flags=all_flags() | f["DELAY"] | nat.CP_FLAG_LAMPORT,
+                        flags=all_flags() | f["DELAY"] | lamport_flags(nat, early),
                         modes=("pipelined", "sequential", "microbatch"), mb_rows=tile[0], reps=2)
     ref = oracle.chain(X, Ws, dtype, acts=list(acts))
     err = oracle.rel_err(as_values(out["pipelined"], dtype), ref)
@@ -248,11 +260,13 @@ def test_lamport_parity(rt, case):
     assert same_bits(out["pipelined"], out["microbatch"])
 
 
+@EARLY
 @pytest.mark.parametrize("dtype", [gen.F32, gen.BF16], ids=["f32", "bf16"])
-def test_lamport_input_negative_zero_is_data(rt, dtype):
+def test_lamport_input_negative_zero_is_data(rt, dtype, early):
     """The caller's X may hold -0.0 (the sentinel's bit pattern): only
     intermediates are checked, so a Lamport run with a third of X set to
-    -0.0 completes (no watchdog) with the sequential mode's bits."""
+    -0.0 completes (no watchdog) with the sequential mode's bits, with and
+    without early dispatch."""
     nat = rt["nat"]
     M, widths = 256, (512, 512, 256)
     X, Ws = gen.chain_inputs(M, widths, dtype, 1.0, (1 / np.sqrt(512), 1 / np.sqrt(512)), 172)
@@ -260,9 +274,15 @@ def test_lamport_input_negative_zero_is_data(rt, dtype):
     neg0 = np.uint16(0x8000) if dtype == gen.BF16 else np.float32(-0.0)
     X.reshape(-1)[::3] = neg0
     tile = (64, 64) if dtype == gen.F32 else (128, 128)
-    out, st = run_modes(rt, X, Ws, dtype, tile, flags=all_flags() | nat.CP_FLAG_LAMPORT,
+    out, st = run_modes(rt, X, Ws, dtype, tile, flags=all_flags() | lamport_flags(nat, early),
                         modes=("pipelined", "sequential"), reps=2)
-    assert st["status"] == 0 and st["lamport_rereads"] == 0, st
+    assert st["status"] == 0, st
+    # released only when stored, no consumer meets a sentinel, so a re-read
+    # here would be X's -0.0 taken for one; with early dispatch consumers do
+    # re-read intermediates still being computed, and finishing without the
+    # watchdog with the sequential bits is what shows that X is not checked
+    if not early:
+        assert st["lamport_rereads"] == 0, st
     assert same_bits(out["pipelined"], out["sequential"])
     assert oracle.rel_err(as_values(out["pipelined"], dtype), oracle.chain(X, Ws, dtype)) <= TOL[dtype]
 

@@ -41,7 +41,7 @@ def test_header_constants_match_binding():
         assert int(m.group(1)) == getattr(nat, name), name
     for name in ("CP_FLAG_DEBUG", "CP_FLAG_TRACE", "CP_FLAG_POISON", "CP_FLAG_DELAY_INJECT",
                  "CP_FLAG_STARVE_LAST", "CP_FLAG_EAGER", "CP_FLAG_COOPERATIVE", "CP_FLAG_FENCE_RELEASE",
-                 "CP_FLAG_TIMING", "CP_FLAG_NO_SPLIT", "CP_FLAG_LAMPORT"):
+                 "CP_FLAG_TIMING", "CP_FLAG_NO_SPLIT", "CP_FLAG_LAMPORT", "CP_FLAG_EARLY_DISPATCH"):
         m = re.search(rf"#define\s+{name}\s+(\d+)u", src)
         assert m and int(m.group(1)) == getattr(nat, name), name
 
@@ -225,6 +225,10 @@ def test_error_codes_without_device():
         nat.cp_chain_plan(128, [512, 512], nat.CP_BF16, 64, 64,
                           flags=nat.CP_FLAG_LAMPORT | nat.CP_FLAG_FENCE_RELEASE)
     assert e.value.code == nat.CP_ERR_INVALID_ARG
+    # early dispatch without the sentinel: consumers would read unstored data
+    with pytest.raises(nat.CpError) as e:
+        nat.cp_chain_plan(128, [512, 512, 512], nat.CP_BF16, 64, 64, flags=nat.CP_FLAG_EARLY_DISPATCH)
+    assert e.value.code == nat.CP_ERR_INVALID_ARG and "LAMPORT" in str(e.value)
     assert nat.error_string(nat.CP_ERR_TIMEOUT)
     assert nat.error_string(12345) == "unknown status"
 

@@ -308,6 +308,8 @@ cp::ChainArgs make_args(const cp_chain *p, const void *X, const void *const *W, 
             if (l + 1 < p->L) d.C = p->lam[copy][l];
             d.lam_in = l > 0 ? 1 : 0;
             d.lam_out = l + 1 < p->L ? 1 : 0;
+            // early dispatch: the arrival counter also counts starts
+            d.arrive_shift = (p->flags & CP_FLAG_EARLY_DISPATCH) && l + 1 < p->L && p->g.nsplit[l] > 1 ? 16 : 0;
         }
         d.tile_off = p->g.layer_off[l];
         d.ntiles = p->g.layer_off[l + 1] - p->g.layer_off[l];
@@ -439,12 +441,15 @@ int cp_chain_plan(cp_chain **out, int64_t M, int32_t n_layers, const int64_t *wi
                 return fail(CP_ERR_INVALID_ARG, "acts[%d] = %d", l, acts[l]);
     const uint32_t known = CP_FLAG_DEBUG | CP_FLAG_TRACE | CP_FLAG_POISON | CP_FLAG_DELAY_INJECT | CP_FLAG_STARVE_LAST |
                            CP_FLAG_EAGER | CP_FLAG_COOPERATIVE | CP_FLAG_FENCE_RELEASE | CP_FLAG_TIMING |
-                           CP_FLAG_NO_SPLIT | CP_FLAG_LAMPORT;
+                           CP_FLAG_NO_SPLIT | CP_FLAG_LAMPORT | CP_FLAG_EARLY_DISPATCH;
     if (flags & ~known) return fail(CP_ERR_INVALID_ARG, "unknown flags 0x%x", flags & ~known);
     if ((flags & CP_FLAG_STARVE_LAST) && n_layers < 2)
         return fail(CP_ERR_INVALID_ARG, "CP_FLAG_STARVE_LAST needs at least two layers");
     if ((flags & CP_FLAG_LAMPORT) && (flags & CP_FLAG_FENCE_RELEASE))
         return fail(CP_ERR_INVALID_ARG, "CP_FLAG_LAMPORT and CP_FLAG_FENCE_RELEASE are two different release protocols");
+    if ((flags & CP_FLAG_EARLY_DISPATCH) && !(flags & CP_FLAG_LAMPORT))
+        return fail(CP_ERR_INVALID_ARG, "CP_FLAG_EARLY_DISPATCH needs CP_FLAG_LAMPORT (consumers started before "
+                                        "their producers finish must find the sentinel in the data)");
 
     int ndev = 0;
     const hipError_t de = hipGetDeviceCount(&ndev);

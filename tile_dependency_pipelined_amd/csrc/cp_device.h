@@ -53,6 +53,13 @@ struct LayerDesc {
                        // for the stores to complete
     int32_t lam_in;    // A is such an intermediate: every A fragment is checked for the
                        // sentinel before use and re-read from memory until it holds none
+    // Split-K arrival counter of a tile (nsplit > 1): an item's completion adds
+    // 1 << arrive_shift, and the item that sees nsplit - 1 earlier completions
+    // is the last.  16 with CP_FLAG_EARLY_DISPATCH when the tile has in-run
+    // consumers: the low 16 bits then count the tile's items as they are
+    // dequeued (the one that sees nsplit - 1 earlier starts queues the
+    // consumers), the high 16 bits their completions.
+    int32_t arrive_shift;
 };
 
 // Everything one launch needs, passed by value as the kernel argument.

@@ -94,6 +94,7 @@ __device__ __forceinline__ void lamport_reread(const uint64_t *src, uint64_t (&v
     const uint64_t t0 = wall_clock64();
     if (w.rereads && (threadIdx.x & 63) == 0)
         __hip_atomic_fetch_add(w.rereads, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t naps = 1;  // back-off, as in the bf16 re-load rounds
     for (;;) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 #pragma unroll
@@ -104,7 +105,8 @@ __device__ __forceinline__ void lamport_reread(const uint64_t *src, uint64_t (&v
                 __hip_atomic_store(w.status, (uint32_t)kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             return;
         }
-        __builtin_amdgcn_s_sleep(2);
+        for (uint32_t n = 0; n < naps; ++n) __builtin_amdgcn_s_sleep(8);
+        if (naps < 16) ++naps;
     }
 }
 
@@ -308,7 +310,11 @@ struct Bf16Body {
                     __hip_atomic_store(lw.status, (uint32_t)kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 break;
             }
-            __builtin_amdgcn_s_sleep(2);
+            // back off: every round's acquire invalidates this XCD's L2 under
+            // the workgroups still computing; a consumer started before its
+            // producers finished (early dispatch) may wait a whole tile here
+            const uint64_t naps = round < 16 ? round + 1 : 16;
+            for (uint64_t n = 0; n < naps; ++n) __builtin_amdgcn_s_sleep(8);
         }
         __syncthreads();
     }
@@ -642,7 +648,8 @@ struct Bf16Body {
             __syncthreads();
             volatile uint32_t *word = reinterpret_cast<volatile uint32_t *>(stg[0]) + 1;
             if (tid == 0)
-                *word = __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                *word = __hip_atomic_fetch_add(arrive, 1u << dp->arrive_shift, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT) >> dp->arrive_shift;
             __syncthreads();
             const bool last = *word == (uint32_t)(dp->nsplit - 1);
             __syncthreads();  // everyone has read the word before the LDS is reused
@@ -995,7 +1002,8 @@ struct F32Body {
             __syncthreads();
             volatile uint32_t *word = reinterpret_cast<volatile uint32_t *>(stg[0]) + 1;
             if (tid == 0)
-                *word = __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                *word = __hip_atomic_fetch_add(arrive, 1u << d.arrive_shift, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT) >> d.arrive_shift;
             __syncthreads();
             const bool last = *word == (uint32_t)(d.nsplit - 1);
             __syncthreads();  // everyone has read the word before the LDS is reused
@@ -1396,6 +1404,30 @@ __device__ __forceinline__ void worker_loop(ChainArgs &a) {
         decode(a, id, l, i, j, split);
         const uint32_t first_item_id = id - (uint32_t)split;  // the tile's first item carries its edges
         bool released = false;
+        // Early dispatch (Lamport plans with CP_FLAG_EARLY_DISPATCH): a
+        // tile's consumers are queued once all its items have started, not
+        // when it is stored.  Each item counts its start in the low half of
+        // the tile's arrival counter; the one that completes the count
+        // queues the consumers (wave 0, right after this item's first loads
+        // are requested).  The tile is then not released when it is stored.
+        const bool early = LAM && (a.flags & CP_FLAG_EARLY_DISPATCH) != 0;
+        bool start_publish = false;
+        if (early && l + 1 < a.L && wave0) {
+            const int ns = a.layer[l].nsplit;
+            if (ns == 1) {
+                start_publish = true;
+            } else {
+                uint32_t old = 0;
+                if (threadIdx.x == 0)
+                    old = __hip_atomic_fetch_add(a.arrive + first_item_id, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+                start_publish = (__builtin_amdgcn_readfirstlane(old) & 0xFFFFu) == (uint32_t)(ns - 1);
+            }
+        }
+        auto after_issue = [&] {
+            release_pending();
+            if (start_publish) publish_edges(a, first_item_id, l);
+        };
         auto next_ticket = [&] {
             if (sched) {
                 ticket = take_ticket(a, q);
@@ -1407,8 +1439,10 @@ __device__ __forceinline__ void worker_loop(ChainArgs &a) {
         auto store_hook = [&] {
             if constexpr (LAM) {
                 if ((a.flags & CP_FLAG_DELAY_INJECT) && l + 1 < a.L && ((first_item_id * 2654435761u) >> 30) == 0) {
-                    publish(a, first_item_id, l);  // release first ...
-                    released = true;
+                    if (!early) {  // (early dispatch: the consumers are queued already)
+                        publish(a, first_item_id, l);  // release first ...
+                        released = true;
+                    }
                     const uint64_t s0 = wall_clock64();
                     while (wall_clock64() - s0 < 2000) __builtin_amdgcn_s_sleep(8);  // ... store ~20 us later
                 }
@@ -1420,10 +1454,10 @@ __device__ __forceinline__ void worker_loop(ChainArgs &a) {
         bool done;
         if (LAM && a.layer[l].lam_in)
             done = Body::template run<SPLIT, true>(a.layer[l], i, j, split, a.arrive + first_item_id, stg, next_ticket,
-                                                   store_hook, release_pending, lw);
+                                                   store_hook, after_issue, lw);
         else
             done = Body::template run<SPLIT, false>(a.layer[l], i, j, split, a.arrive + first_item_id, stg,
-                                                    next_ticket, store_hook, release_pending, lw);
+                                                    next_ticket, store_hook, after_issue, lw);
         if (a.trace && threadIdx.x == 0) {
             a.trace[kTraceWords * (size_t)id + 2] = wall_clock64();
             a.trace[kTraceWords * (size_t)id + 5] = clock64();
@@ -1431,7 +1465,7 @@ __device__ __forceinline__ void worker_loop(ChainArgs &a) {
         // a split-K item that did not complete its tile has nothing to
         // release; a completed one is released now, or, if the next tile is
         // already there, right after that tile's first loads are requested
-        if (done && l + 1 < a.L && !released) {
+        if (done && l + 1 < a.L && !released && !early) {
             release_stores(a, l);
             if (wave0) {
                 if (__builtin_amdgcn_readfirstlane(peek)) {

@@ -33,6 +33,7 @@ CP_FLAG_FENCE_RELEASE = 128
 CP_FLAG_TIMING = 256
 CP_FLAG_NO_SPLIT = 512
 CP_FLAG_LAMPORT = 1024
+CP_FLAG_EARLY_DISPATCH = 2048
 CP_MAX_LAYERS = 8
 
 # every symbol include/cp_chain.h declares
