@@ -37,6 +37,18 @@
 // the same integer chain (mod 2^64).  --starve raises the last item's
 // in-degree by one: the run must end through the watchdog with
 // CP_ERR_TIMEOUT, every worker exiting, and only that item never dequeued.
+//
+// --early models CP_FLAG_EARLY_DISPATCH of Lamport plans: a producer tile's
+// consumers are queued once every item of the tile has been dequeued (the
+// low half of the tile's arrival word counts starts, the high half
+// completions), and a consumer waits, per producer tile it reads, until the
+// tile is stored.  On the GPU the wait is the sentinel check and re-read of
+// the data after an agent-scope acquire; here it is a per-copy "stored" word
+// per tile, written with release after the tile's data and polled with
+// acquire (with the watchdog) before the data is read, so TSan still reports
+// any read of a tile not ordered after its write.  The order check then
+// requires every consumer to start after every item of each of its producer
+// tiles started, and few workers (down to one) must still finish.
 #include <algorithm>
 #include <atomic>
 #include <chrono>
@@ -99,16 +111,16 @@ Graph read_graph(const char *path) {
 
 // one copy of the per-run state, as the plan allocates it twice
 struct State {
-    std::vector<std::atomic<uint32_t>> queue, arrive, deq;
+    std::vector<std::atomic<uint32_t>> queue, arrive, deq, stored;
     std::vector<std::atomic<int32_t>> score;
     std::atomic<uint32_t> ctl[kCtlWords];
     std::vector<uint64_t> start_seq, release_seq;  // order check (the kernel's trace stamps)
-    explicit State(int T) : queue(T), arrive(T), deq(T), score(T), start_seq(T), release_seq(T) {}
+    explicit State(int T) : queue(T), arrive(T), deq(T), stored(T), score(T), start_seq(T), release_seq(T) {}
 };
 
 struct Config {
     int nworkers = 16, nq = 8, runs = 4;
-    bool spatial = false, starve = false;
+    bool spatial = false, starve = false, early = false;
     uint64_t seed = 1;
     int delay_us = 20;        // upper bound of an injected delay
     int delay_pct = 25;       // chance of a delay at each delay point
@@ -116,7 +128,8 @@ struct Config {
     // a planted mistake (tests of the simulator itself): 1 consumer load
     // relaxed instead of acquire, 2 producer decrements relaxed instead of
     // release, 3 split-K arrival relaxed, 4 exit-time reset skipped, 5 first
-    // slots computed one item off
+    // slots computed one item off, 6 (early dispatch) consumers queued when
+    // the first item of a split producer tile starts, not the last
     int plant = 0;
 };
 
@@ -222,6 +235,7 @@ struct Sim {
             s.queue[t].store(qinit[t], std::memory_order_relaxed);
             s.arrive[t].store(0, std::memory_order_relaxed);
             s.deq[t].store(0, std::memory_order_relaxed);
+            s.stored[t].store(0, std::memory_order_relaxed);
         }
         if (w == 0) {
             for (int i = 0; i < kCtlWords; ++i) s.ctl[i].store(0, std::memory_order_relaxed);
@@ -298,14 +312,35 @@ struct Sim {
         j = tile - i * g.nbn[l];
     }
 
+    // early dispatch: wait until producer tile (l, i, k) is stored (the
+    // sentinel check); false if the watchdog ended the run
+    bool wait_stored(State &s, int l, int i, int k) {
+        const uint32_t t = (uint32_t)(g.layer_off[l] + (i * g.nbn[l] + k) * g.nsplit[l]);  // its first item
+        const auto t0 = std::chrono::steady_clock::now();
+        uint32_t polls = 0;
+        while (s.stored[t].load(std::memory_order_acquire) == 0) {
+            std::this_thread::yield();
+            if ((++polls & 63) == 0) {
+                if (std::chrono::steady_clock::now() - t0 > std::chrono::milliseconds(cfg.timeout_ms)) {
+                    s.ctl[cp::kCtlStatus].store((uint32_t)cp::kStatusTimeout, std::memory_order_relaxed);
+                    return false;
+                }
+                if (s.ctl[cp::kCtlStatus].load(std::memory_order_relaxed) != 0) return false;
+            }
+        }
+        return true;
+    }
+
     // the tile body: item (l, i, j, split) over its k range; layer 0 reads
     // the (constant) input, later layers the producers' outputs (plain reads)
-    uint64_t body(int l, int i, int j, int split) {
+    uint64_t body(State &s, int l, int i, int j, int split) {
         if (l == 0) return mix(((uint64_t)i << 40) ^ ((uint64_t)j << 20) ^ (uint64_t)split);
         const int per = g.nbn[l - 1] / g.nsplit[l];
         uint64_t acc = 0;
-        for (int k = split * per; k < (split + 1) * per; ++k)
+        for (int k = split * per; k < (split + 1) * per; ++k) {
+            if (cfg.early && !wait_stored(s, l - 1, i, k)) return 0;
             acc += C[l - 1][(size_t)i * g.nbn[l - 1] + k] * weight(l, k, j);
+        }
         return acc;
     }
 
@@ -359,14 +394,26 @@ struct Sim {
             int l, i, j, split;
             decode(id, l, i, j, split);
             const uint32_t first_item_id = id - (uint32_t)split;
-            uint64_t acc = body(l, i, j, split);
+            const int ns = g.nsplit[l];
+            // early dispatch: the last item of the tile to start queues its
+            // consumers (the GPU does it once its first loads are issued)
+            const int shift = cfg.early && l + 1 < g.L && ns > 1 ? 16 : 0;
+            if (cfg.early && l + 1 < g.L) {
+                bool last_start = true;
+                if (ns > 1) {
+                    const uint32_t old = s.arrive[first_item_id].fetch_add(1, std::memory_order_relaxed);
+                    last_start = (old & 0xFFFFu) == (uint32_t)(cfg.plant == 6 ? 0 : ns - 1);
+                }
+                if (last_start) publish(s, first_item_id, l, rng);
+            }
+            uint64_t acc = body(s, l, i, j, split);
             ticket = take_ticket(s, q);  // the scheduler lane, during the epilogue
             rng.delay();
             bool done = true;
             if (g.nsplit[l] > 1) {
                 P[l][id - g.layer_off[l]] = acc;
                 const uint32_t old = s.arrive[first_item_id].fetch_add(
-                    1, cfg.plant == 3 ? std::memory_order_relaxed : std::memory_order_acq_rel);
+                    1u << shift, cfg.plant == 3 ? std::memory_order_relaxed : std::memory_order_acq_rel) >> shift;
                 if (old != (uint32_t)g.nsplit[l] - 1) {
                     done = false;
                 } else {
@@ -376,8 +423,9 @@ struct Sim {
                 }
             }
             if (done) C[l][(size_t)i * g.nbn[l] + j] = acc;
+            if (done && cfg.early) s.stored[first_item_id].store(1, std::memory_order_release);
             rng.delay();
-            if (done && l + 1 < g.L) publish(s, first_item_id, l, rng);
+            if (done && l + 1 < g.L && !cfg.early) publish(s, first_item_id, l, rng);
         }
         if (cfg.plant != 4) reset_share(nxt, w, cfg.nworkers);
     }
@@ -470,9 +518,19 @@ struct Sim {
         if (bad_deq) die("run %s%lld: %lld items not dequeued exactly once", "", r, bad_deq);
         int viol = 0;
         for (int p = 0; p < g.T; ++p)
-            for (int e = g.dep_off[p]; e < g.dep_off[p + 1]; ++e)
-                viol += s.start_seq[g.dep_ids[e]] < s.release_seq[p];
-        if (viol) die("run %s%lld: %lld consumers started before a producer released", "", r, viol);
+            for (int e = g.dep_off[p]; e < g.dep_off[p + 1]; ++e) {
+                if (!cfg.early) {
+                    viol += s.start_seq[g.dep_ids[e]] < s.release_seq[p];
+                } else {
+                    // every item of producer tile p (p is its first item) started first
+                    int l = 0;
+                    while (l + 1 < g.L && p >= g.layer_off[l + 1]) ++l;
+                    for (int k = 0; k < g.nsplit[l]; ++k) viol += s.start_seq[g.dep_ids[e]] < s.start_seq[p + k];
+                }
+            }
+        if (viol)
+            die(cfg.early ? "run %s%lld: %lld consumers started before a producer item started"
+                          : "run %s%lld: %lld consumers started before a producer released", "", r, viol);
         const std::vector<uint64_t> &y = C[g.L - 1];
         for (size_t k = 0; k < y.size(); ++k)
             if (y[k] != ref[k]) die("run %s%lld: output element %lld differs from the sequential chain", "", r, (long long)k);
@@ -486,7 +544,7 @@ struct Sim {
 int main(int argc, char **argv) {
     if (argc < 2) {
         std::fprintf(stderr, "usage: %s GRAPH [--workers N] [--queues N] [--runs N] [--seed S] [--delay-us D] "
-                             "[--delay-pct P] [--spatial] [--starve] [--timeout-ms T]\n", argv[0]);
+                             "[--delay-pct P] [--spatial] [--starve] [--early] [--timeout-ms T]\n", argv[0]);
         return 2;
     }
     Sim sim;
@@ -506,6 +564,7 @@ int main(int argc, char **argv) {
         else if (k == "--timeout-ms") sim.cfg.timeout_ms = (int)val();
         else if (k == "--spatial") sim.cfg.spatial = true;
         else if (k == "--starve") sim.cfg.starve = true;
+        else if (k == "--early") sim.cfg.early = true;
         else if (k == "--plant") sim.cfg.plant = (int)val();
         else die("unknown option %s", k.c_str());
     }

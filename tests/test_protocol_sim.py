@@ -8,7 +8,8 @@ the library's own host builder (cp_chain_tile_graph_split).  Each run must
 terminate with every invariant exact and the same output as a sequential
 evaluation, and TSan must report no data race on the tile data.  Planted
 protocol mistakes (weakened memory orders, a skipped reset, a wrong first
-slot) must each be caught."""
+slot) must each be caught.  --early runs the same protocol with early
+dispatch (Lamport plans' CP_FLAG_EARLY_DISPATCH)."""
 import os
 import subprocess
 
@@ -108,6 +109,45 @@ def test_watchdog_ends_a_starved_run(sim, spatial):
                            "--workers", 16, "--runs", 2, *extra)
     assert rc == 0, err[-4000:]
     assert out.count("timed out, all 16 workers exited") == 2, out
+
+
+@pytest.mark.parametrize("name", ["fp32 128x512x512x512, split 4", "256x8192x28672x8192, layer 2 split 4",
+                                  "eight layers, mixed splits", "three layers, every layer split"])
+def test_early_dispatch_exact_under_tsan(sim, name):
+    """Early dispatch (Lamport plans): consumers queued once every item of
+    each producer tile has started, then waiting per producer tile for its
+    store: every invariant exact, output equal to the sequential chain, no
+    data race on the tile data, every consumer started after all items of
+    its producer tiles."""
+    rc, out, err = run_sim(sim, name, "--early", "--workers", 24, "--queues", 8, "--runs", 4, "--seed", 11,
+                           "--delay-us", 30, "--delay-pct", 30)
+    assert rc == 0, err[-4000:]
+    assert out.count(": ok,") == 4, out
+
+
+@pytest.mark.parametrize("workers", [1, 2, 3, 8])
+def test_early_dispatch_few_workers(sim, workers):
+    """Deadlock freedom of early dispatch with fewer workers than items (down
+    to one): an item is queued only when all its producers are on workers,
+    so a waiting consumer never holds the worker a producer needs."""
+    rc, out, err = run_sim(sim, "three layers, every layer split", "--early", "--workers", workers, "--runs", 3,
+                           "--seed", 13, "--delay-us", 20, "--delay-pct", 30)
+    assert rc == 0, err[-4000:]
+    assert out.count(": ok,") == 3, out
+
+
+def test_planted_early_dispatch_mistake_is_caught(sim):
+    """Early dispatch that queues a split tile's consumers when its first
+    item starts (not its last): a consumer may start before a producer item
+    does, and with few workers wait for a tile whose remaining items sit
+    behind it in the queue; the order check or the watchdog must catch it."""
+    for workers, seed in ((2, 3), (4, 5), (8, 7)):
+        rc, out, err = run_sim(sim, "three layers, every layer split", "--early", "--plant", 6, "--workers", workers,
+                               "--runs", 3, "--seed", seed, "--timeout-ms", 300)
+        if rc != 0:
+            assert "FAIL:" in err or "ThreadSanitizer" in err, err[-2000:]
+            return
+    pytest.fail("planted early-dispatch mistake not caught\n" + out)
 
 
 @pytest.mark.parametrize("plant, what", [
