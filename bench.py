@@ -225,25 +225,29 @@ def main():
         # the Lamport-sentinel release is a plan of its own too; the
         # micro-batched baseline needs at least two row chunks, and where the
         # timed tile spans the whole batch it runs on a plan of lower tiles
+        # (a failure here is reported in the line; the headline above stands)
         mb_tile = tuning.microbatch_tile(cfg.M, tile)
-        with ch.Chain(cfg.M, cfg.widths, cfg.dtype, tile[0], tile[1], acts=list(cfg.acts)) as sp, \
-                ch.Chain(cfg.M, cfg.widths, cfg.dtype, tile[0], tile[1], acts=list(cfg.acts),
-                         flags=nat.CP_FLAG_LAMPORT) as lp, \
-                ch.Chain(cfg.M, cfg.widths, cfg.dtype, tile[0], tile[1], acts=list(cfg.acts),
-                         flags=nat.CP_FLAG_LAMPORT | nat.CP_FLAG_EARLY_DISPATCH) as lep, \
-                ch.Chain(cfg.M, cfg.widths, cfg.dtype, mb_tile[0], mb_tile[1], acts=list(cfg.acts)) as mp:
-            def step_modes(mode="pipelined", mb=0):
-                if mode == "lamport":
-                    step("pipelined", 0, p=lp)
-                elif mode == "lamport_early":
-                    step("pipelined", 0, p=lep)
-                elif mode == "microbatch":
-                    step(mode, mb, p=mp if mb_tile != tile else plan)
-                else:
-                    step(mode, mb, p=sp if mode == "spatial" else plan)
-            result["modes"] = compare_modes(plan, step_modes, stream, cfg, mb_tile, args.reps, torch, tuning)
-            if mb_tile != tile:
-                result["modes"]["microbatch_tile"] = list(mb_tile)
+        try:
+            with ch.Chain(cfg.M, cfg.widths, cfg.dtype, tile[0], tile[1], acts=list(cfg.acts)) as sp, \
+                    ch.Chain(cfg.M, cfg.widths, cfg.dtype, tile[0], tile[1], acts=list(cfg.acts),
+                             flags=nat.CP_FLAG_LAMPORT) as lp, \
+                    ch.Chain(cfg.M, cfg.widths, cfg.dtype, tile[0], tile[1], acts=list(cfg.acts),
+                             flags=nat.CP_FLAG_LAMPORT | nat.CP_FLAG_EARLY_DISPATCH) as lep, \
+                    ch.Chain(cfg.M, cfg.widths, cfg.dtype, mb_tile[0], mb_tile[1], acts=list(cfg.acts)) as mp:
+                def step_modes(mode="pipelined", mb=0):
+                    if mode == "lamport":
+                        step("pipelined", 0, p=lp)
+                    elif mode == "lamport_early":
+                        step("pipelined", 0, p=lep)
+                    elif mode == "microbatch":
+                        step(mode, mb, p=mp if mb_tile != tile else plan)
+                    else:
+                        step(mode, mb, p=sp if mode == "spatial" else plan)
+                result["modes"] = compare_modes(plan, step_modes, stream, cfg, mb_tile, args.reps, torch, tuning)
+                if mb_tile != tile:
+                    result["modes"]["microbatch_tile"] = list(mb_tile)
+        except Exception as e:
+            result["modes"] = {"error": f"{type(e).__name__}: {e}"[:300]}
 
     if not args.profile:
         result["gpu_state_after_timed_steps"] = gpu_state()
