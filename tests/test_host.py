@@ -315,3 +315,20 @@ def test_graph_size_overflow_rejected(M, widths, nsplit):
         with pytest.raises(nat.CpError) as e:
             nat.cp_chain_plan(M, widths, nat.CP_BF16, 64, 64)
         assert e.value.code == nat.CP_ERR_SHAPE
+
+
+def test_microbatch_chunks_and_tile():
+    """The micro-batched baseline needs at least two row chunks, each a
+    multiple of the tile height that divides M; where the timed tile spans
+    the batch (256-row tiles on a 256-row batch) its plan takes tiles of half
+    the height."""
+    from tile_dependency_pipelined_amd import inputs as gen, tuning
+    assert tuning.chunk_sweep(2048, 256) == [256, 512, 1024]
+    assert tuning.chunk_sweep(256, 256) == []
+    assert tuning.microbatch_tile(256, (256, 128)) == (128, 128)
+    assert tuning.microbatch_tile(2048, (256, 256)) == (256, 256)
+    for key, tile in tuning.TILES.items():
+        cfg = gen.CONFIGS[key]
+        mb = tuning.microbatch_tile(cfg.M, tile)
+        chunks = tuning.chunk_sweep(cfg.M, mb[0])
+        assert chunks and all(cfg.M % c == 0 and c % mb[0] == 0 and c < cfg.M for c in chunks), (key, mb, chunks)
