@@ -175,6 +175,28 @@ def summarize(args):
     lds_wait = pmc("SQ_WAIT_INST_LDS")
     if lds_wait is not None and wave:
         kv["derived_wave_lds_issue_wait_frac"] = f"{lds_wait / wave:.3f}"
+    # each CU's vector L1 -> L2 reads (TCP counters summed over the CUs;
+    # GRBM_GUI_ACTIVE summed over the XCDs, so GUI / XCDS is the launch's
+    # cycles): mean latency, reads in flight per CU (Little's law: latency
+    # sum over cycles), bytes per cycle per CU (128-byte reads), and the
+    # fraction of cycles a CU's L1 waited for data from the L2
+    gui = pmc("GRBM_GUI_ACTIVE")
+    rq, lat = pmc("TCP_TCC_READ_REQ_sum"), pmc("TCP_TCC_READ_REQ_LATENCY_sum")
+    cyc = gui / args.xcds if gui else None
+    if rq and lat is not None:
+        kv["derived_cu_l2_read_latency_cycles"] = f"{lat / rq:.0f}"
+        if cyc:
+            kv["derived_cu_l2_reads_in_flight_per_cu"] = f"{lat / (args.cus * cyc):.1f}"
+            kv["derived_cu_l2_read_bytes_per_cycle_per_cu"] = f"{rq * 128 / (args.cus * cyc):.1f}"
+    pend = pmc("TCP_PENDING_STALL_CYCLES_sum")
+    if pend is not None and cyc:
+        kv["derived_cu_l1_pending_stall_frac"] = f"{pend / (args.cus * cyc):.3f}"
+    # the L2's reads from memory (TCC counters summed over the channels)
+    erq, elev = pmc("TCC_EA0_RDREQ_sum"), pmc("TCC_EA0_RDREQ_LEVEL_sum")
+    if erq and elev is not None:
+        kv["derived_l2_mem_read_latency_cycles"] = f"{elev / erq:.0f}"
+        if cyc:
+            kv["derived_l2_mem_reads_in_flight_per_xcd"] = f"{elev / cyc / args.xcds:.0f}"
     if "fetch_bytes_per_launch" in kv and "write_bytes_per_launch" in kv:
         kv["hbm_bytes_per_launch"] = str(int(float(kv["fetch_bytes_per_launch"]) +
                                              float(kv["write_bytes_per_launch"])))
@@ -201,6 +223,8 @@ def main(argv=None):
                    help="further counter_collection.csv files; the worker kernel's median per "
                         "dispatch of every counter in them is recorded")
     s.add_argument("--cmd", action="append", default=[])
+    s.add_argument("--cus", type=int, default=256, help="compute units (MI355X: 256)")
+    s.add_argument("--xcds", type=int, default=8, help="XCDs (MI355X: 8)")
     s.add_argument("--out", required=True)
     args = ap.parse_args(argv)
     summarize(args)
