@@ -84,6 +84,10 @@ def main():
     t0 = time.time()
     X, Ws = gen.config_inputs(cfg)
     log(f"inputs generated in {time.time() - t0:.1f}s")
+    # SHA-256 of the exact bytes handed to the device (bf16 bit patterns or
+    # fp32), so that a line can be tied to its inputs
+    inputs_sha256 = {name: hashlib.sha256(np.ascontiguousarray(a).view(np.uint8)).hexdigest()
+                     for name, a in [("X", X)] + [(f"W{l + 1}", w) for l, w in enumerate(Ws)]}
     dX = ch.to_device(X, cfg.dtype)
     dW = [ch.to_device(w, cfg.dtype) for w in Ws]
     dY = torch.empty((cfg.M, cfg.widths[-1]), dtype=ch.DTYPES[cfg.dtype], device="cuda")
@@ -185,7 +189,7 @@ def main():
         "data": "synthetic (seeded N(0, sigma^2), PCG64)",
         "config": {"workload": cfg.description, "key": cfg.key, "M": cfg.M,
                    "widths": list(cfg.widths), "tile": list(tile), "mode": "pipelined",
-                   "workers": plan.n_workers, "tiles": plan.n_tiles},
+                   "workers": plan.n_workers, "tiles": plan.n_tiles, "inputs_sha256": inputs_sha256},
         "wall_ms_per_step": round(wall_ms, 4),
         "settle": settle,
         "per_step_check": per_step,
