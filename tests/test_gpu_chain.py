@@ -675,3 +675,40 @@ def test_intermediate_readback_matches_prefix_chain(rt):
     assert same_bits(c1, ch.to_host(d1, gen.BF16))
     ref, hs = oracle.chain(X, Ws, gen.BF16, acts=[gen.ACT_GELU_TANH, gen.ACT_NONE], return_intermediates=True)
     assert oracle.rel_err(as_values(c1, gen.BF16), hs[0]) <= TOL[gen.BF16]
+
+
+@pytest.mark.parametrize("case", [
+    ("split-K fp32, 64x64", 128, (512, 512, 512), gen.F32, (64, 64), [0, 0]),
+    ("four layers with GeLU, 128x128", 256, (1024, 2048, 1024, 2048, 512), gen.BF16, (128, 128), [0, 1, 0, 0]),
+    ("first-layer backlog, deferred releases, 64x64", 8192, (512, 512, 512, 512), gen.BF16, (64, 64), [0, 0, 0]),
+], ids=lambda c: c[0])
+def test_repeated_runs_exact_every_protocol(rt, case):
+    """One plan per release protocol (write-through, fence, Lamport,
+    Lamport with early dispatch) runs the pipelined chain 100 times: every
+    run keeps every invariant (counters 0, one dequeue per tile, queues a
+    permutation and drained, no consumer dequeued before a producer
+    released) and gives the sequential run's output bit for bit, so a race
+    that shows only now and then in the protocol fails here."""
+    torch, ch, nat = rt["torch"], rt["chain"], rt["nat"]
+    name, M, widths, dtype, tile, acts = case
+    say(name, "M", M, "widths", widths, "tile", tile)
+    stds = tuple(1 / np.sqrt(w) for w in widths[:-1])
+    X, Ws = gen.chain_inputs(M, widths, dtype, 1.0, stds, 88)
+    dX, dW = ch.to_device(X, dtype), [ch.to_device(w, dtype) for w in Ws]
+    dY = torch.empty((M, widths[-1]), dtype=ch.DTYPES[dtype], device="cuda")
+    with ch.Chain(M, widths, dtype, tile[0], tile[1], acts=acts) as c:
+        c.run(dX, dW, dY, mode="sequential")
+        c.stats()
+        ref = ch.to_host(dY, dtype)
+    dbg = rt_flags()["DEBUG"] | rt_flags()["TRACE"]
+    for pname, pf in (("write-through", 0), ("fence", nat.CP_FLAG_FENCE_RELEASE),
+                      ("lamport", lamport_flags(nat, False)), ("lamport, early", lamport_flags(nat, True))):
+        say(name, pname)
+        with ch.Chain(M, widths, dtype, tile[0], tile[1], acts=acts, flags=dbg | pf) as c:
+            for r in range(100):
+                dY.fill_(float("nan"))
+                c.run(dX, dW, dY)
+                st = c.stats()
+                assert st["status"] == 0, (pname, r, st)
+                check_invariants(st, dbg)
+                assert same_bits(ch.to_host(dY, dtype), ref), (pname, r)
