@@ -207,12 +207,20 @@ def main():
         del a, b
 
     traffic = traffic_from_profile(cfg.key, tile)
+    # each CU's reads from the L2 in the same committed summary (what bounds
+    # the tile bodies here: reads in flight over their latency), or None
+    from tile_dependency_pipelined_amd import profiling
+    read_path = profiling.load_figures(os.path.join(ROOT, "profiles"), cfg.key, tile, (
+        "derived_cu_l2_read_latency_cycles", "derived_cu_l2_reads_in_flight_per_cu",
+        "derived_cu_l2_read_bytes_per_cycle_per_cu", "derived_cu_l1_pending_stall_frac",
+        "derived_l2_hit_rate"))
     bound, achieved, peak_b, unit, intensity = roofline(flops, cfg.min_bytes(), kernel_ms, peak)
     result["roofline"] = {
         "bound": bound, "achieved": round(achieved, 2), "peak": peak_b, "unit": unit,
         "frac": round(achieved / peak_b, 4), "tflops": round(kernel_tflops, 2),
         "arithmetic_intensity_flop_per_byte": round(intensity, 1),
         "traffic": traffic,
+        "cu_l2_read_path": ({k.replace("derived_", ""): v for k, v in read_path.items()} if read_path else None),
         "kernel": "cp::worker_kernel<Bf16Body<%d,%d,...>>" % tile if cfg.dtype == gen.BF16 else "worker_kernel<F32Body>",
         "kernel_us": round(kernel_ms * 1e3, 1),
         "kernel_us_isolated_median": None if iso_ms != iso_ms else round(iso_ms * 1e3, 1),

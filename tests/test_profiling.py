@@ -43,12 +43,15 @@ def test_traffic_is_scaled_by_the_copy(tmp_path):
     # the summary carries the current sources' hash, so the bench can use it
     os.rename(out, tmp_path / "worker_c3_256x256.md")
     assert pf.load_traffic(str(tmp_path), "c3", (256, 256)) == 1000 * 1024 * 2 + 300 * 1024
+    figs = pf.load_figures(str(tmp_path), "c3", (256, 256), ("fetch_scale", "write_scale", "absent"))
+    assert figs == {"fetch_scale": 2.0, "write_scale": 1.0}
 
 
 def test_summary_of_other_sources_is_ignored(tmp_path):
     p = tmp_path / "worker_c3_256x256.md"
     p.write_text("- kernel_source_sha256: 0000\n- hbm_bytes_per_launch: 123\n")
     assert pf.load_traffic(str(tmp_path), "c3", (256, 256)) is None
+    assert pf.load_figures(str(tmp_path), "c3", (256, 256), ("hbm_bytes_per_launch",)) is None
     assert pf.load_traffic(str(tmp_path), "c5", (256, 128)) is None  # absent
 
 

@@ -67,6 +67,24 @@ def load_traffic(profiles_dir, workload, tile):
         return None
 
 
+def load_figures(profiles_dir, workload, tile, keys):
+    """{key: float} of the named figures of a summary taken on the current
+    sources (keys absent from it are left out), or None."""
+    path = traffic_path(profiles_dir, workload, tile)
+    if not os.path.exists(path):
+        return None
+    kv = parse_kv(path)
+    if kv.get("kernel_source_sha256") != kernel_source_sha256():
+        return None
+    out = {}
+    for k in keys:
+        try:
+            out[k] = float(kv[k])
+        except (KeyError, ValueError):
+            pass
+    return out
+
+
 def read_csv(path):
     with open(path, newline="") as f:
         return list(csv.DictReader(f))
