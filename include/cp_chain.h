@@ -12,7 +12,8 @@
  * tile of layer l that it reads has been stored, instead of waiting for a
  * kernel boundary (§III, execution model; Fig. 1).  Readiness is tracked by a
  * host-built dependency array, a device scoreboard of atomic counters that
- * producer epilogues decrement after a release fence, and a work-queue into
+ * producer epilogues decrement once their stores are released (see
+ * CP_FLAG_FENCE_RELEASE for the two ways), and a work-queue into
  * which the producer that completes a consumer's count pushes the consumer's
  * tile ID; a consumer prologue takes queue slots in order and remaps its
  * workgroup to the tile it dequeued (§III-A "dependency structure"; the
@@ -110,9 +111,9 @@ typedef struct cp_chain cp_chain; /* opaque plan */
  * keeps two copies of the intermediates, pre-filled with the sentinel -0.0
  * (each run's workers fill the copy the next run uses); producers store
  * their tiles with -0.0 replaced by +0.0 and decrement the counters
- * without waiting for their stores to complete; consumers check every A
- * fragment they read for the sentinel and re-read it from memory until it
- * holds none.  Y is bit for bit that of every other mode.  Not with
+ * without waiting for their stores to complete; consumers check the A data
+ * they load for the sentinel (bf16: every slab as it lands in LDS; fp32:
+ * every fragment) and re-load it from memory until it holds none.  Y is bit for bit that of every other mode.  Not with
  * CP_FLAG_FENCE_RELEASE (CP_ERR_INVALID_ARG); CP_MODE_SPATIAL runs of such a
  * plan return CP_ERR_UNSUPPORTED.  With CP_FLAG_DELAY_INJECT a quarter of
  * producers release their tile before storing it (stored ~20 us later), so
