@@ -712,3 +712,48 @@ def test_repeated_runs_exact_every_protocol(rt, case):
                 assert st["status"] == 0, (pname, r, st)
                 check_invariants(st, dbg)
                 assert same_bits(ch.to_host(dY, dtype), ref), (pname, r)
+
+
+@pytest.mark.parametrize("case", [
+    ("output row of 2^22 elements", 64, (64, 1 << 22), (64, 128)),
+    ("contraction of 2^22 elements, split-K", 64, (1 << 22, 128, 128), (64, 128)),
+], ids=lambda c: c[0])
+def test_maximum_widths(rt, case):
+    """Widths at the plan's limit (2^22 elements per row): the per-lane
+    32-bit offsets of the direct loads (row x width x 2 bytes) and the
+    buffer ranges are at their largest.  Pipelined and sequential give the
+    same bits, and the oracle agrees: on 2048 sampled columns and the last
+    tile's columns of the wide output (one layer, columns independent), on
+    every element of the long-contraction chain."""
+    torch, ch, nat = rt["torch"], rt["chain"], rt["nat"]
+    name, M, widths, tile = case
+    say(name, "M", M, "widths", widths, "tile", tile, "generating inputs")
+    stds = tuple(1 / np.sqrt(w) for w in widths[:-1])
+    X, Ws = gen.chain_inputs(M, widths, gen.BF16, 1.0, stds, 89)
+    dX, dW = ch.to_device(X, gen.BF16), [ch.to_device(w, gen.BF16) for w in Ws]
+    out = {}
+    with ch.Chain(M, widths, gen.BF16, tile[0], tile[1], flags=rt_flags()["DEBUG"]) as c:
+        for mode in ("pipelined", "sequential"):
+            say(name, "running", mode)
+            dY = torch.full((M, widths[-1]), float("nan"), dtype=torch.bfloat16, device="cuda")
+            c.run(dX, dW, dY, mode=mode)
+            st = c.stats()
+            assert st["status"] == 0, st
+            if mode == "pipelined":
+                check_invariants(st, rt_flags()["DEBUG"])
+            out[mode] = dY
+    assert torch.equal(out["pipelined"].view(torch.int16), out["sequential"].view(torch.int16))
+    Y = out["pipelined"]
+    if len(widths) == 2:
+        rng = np.random.default_rng(5)
+        cols = np.concatenate([np.sort(rng.choice(widths[1] - tile[1], 2048, replace=False)),
+                               np.arange(widths[1] - tile[1], widths[1])])
+        got = ch.to_host(Y[:, torch.as_tensor(cols, device="cuda")].contiguous(), gen.BF16)
+        ref = oracle.chain(X, [np.ascontiguousarray(Ws[0][:, cols])], gen.BF16)
+    else:
+        say(name, "oracle over all", M, "rows")
+        got = ch.to_host(Y, gen.BF16)
+        ref = oracle.chain(X, Ws, gen.BF16)
+    err = oracle.rel_err(as_values(got, gen.BF16), ref)
+    say(name, "rel err", err)
+    assert err <= TOL[gen.BF16]
